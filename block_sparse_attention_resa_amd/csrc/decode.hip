@@ -1,0 +1,286 @@
+// Split-K flash decode over a block list: group block sparse attention
+// (selected blocks) and dense attention (all blocks).
+//
+// "Rectified Sparse Attention" analysis page (paper-graph-ui): §3.4.1 Eq 1
+// (GQA attention) and Eq 2 (attention restricted to the selected blocks,
+// masked positions excluded from the softmax), §3.4.4 (split execution over
+// the GPU with partial log-sum-exp results combined afterwards, and one load
+// of each KV block per GQA group shared by all of its query heads).
+//
+// Work decomposition.  Grid (splits, KV heads, requests).  The block list of
+// one (request, KV head) is cut into `splits` equal ranges, one per
+// 256-thread workgroup; the workgroup's four wavefronts take consecutive
+// sub-ranges and each keeps its own online-softmax state, merged through LDS
+// at the end into one partial (m, l, o) per query head.  A second kernel
+// merges the splits' partials with their log-sum-exp weights.
+//
+// Matrix cores.  Per 16-token block a wavefront computes the transposed score
+// tile S^T (16 tokens x 16 query-head columns, g <= 16 of them used) as
+// K . Q^T with v_mfma_f32_16x16x32_bf16 (16x16x4_f32 for fp32 caches), then
+// O^T (channels x heads) += V^T . P^T with v_mfma_f32_16x16x16_bf16.  The S^T
+// accumulator layout (lane l: tokens 4*(l/16)+e, column l%16) is exactly the
+// B-operand layout of the second product, so P never leaves registers.  The
+// value pool stores each block channel-major ([d][16]), which makes the
+// V^T A-operand four consecutive tokens of one channel: one 8-byte load.
+// Keys are token-major, and a lane's four 16-byte K loads are contiguous
+// because the contraction index is permuted identically in K and Q.
+//
+// P is split into a bf16 high part and a bf16 residual (p - hi) and both are
+// multiplied by V, so the probabilities enter the matrix product with about
+// 16 significant bits; a plain bf16 P would contribute a relative error of
+// about 1e-3 to the output on its own.
+//
+// Data movement.  Every byte of K and V is used by exactly one wavefront, so
+// operands go from HBM straight into VGPRs in MFMA layout; the next chunk's
+// loads are issued before the current chunk is computed.  Block ids and
+// physical ids for up to 64 positions are fetched with one vector load each
+// and broadcast with readlane.  Rows past the sequence end are masked by
+// selection (score -> -inf, value -> 0), so any bit pattern there is harmless.
+#include "attn_frag.h"
+#include "resa_internal.h"
+
+namespace resa {
+namespace {
+
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+constexpr int kChunk = 2;  // blocks per pipelined chunk
+
+template <typename T, int D>
+struct Chunk {
+  typename Frag<T, D>::KV f[kChunk];
+  int blk[kChunk];  // logical block id, -1 = empty slot
+};
+
+template <typename T, int D, bool SPARSE>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ k_pool, const T* __restrict__ v_pool,
+    const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_idx,
+    const int32_t* __restrict__ sel_cnt, int max_sel, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int H, int G, int max_blocks, int num_pool_blocks, int S, float scale_log2) {
+  using F = Frag<T, D>;
+  constexpr int NT = F::NT;
+  __shared__ float s_acc[kDecodeWaves][16][D + 4];
+  __shared__ float s_m[kDecodeWaves][16];
+  __shared__ float s_l[kDecodeWaves][16];
+
+  const int s = blockIdx.x;
+  const int i = blockIdx.y;
+  const int r = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+
+  const int L = clampi(seq_lens[r], 0, max_blocks * kBlock);
+  const int M = (L + kBlock - 1) / kBlock;
+  int n, bps;
+  if (SPARSE) {
+    n = clampi(sel_cnt[(size_t)r * H + i], 0, max_sel < M ? max_sel : M);
+    bps = (max_sel + S - 1) / S;
+  } else {
+    n = M;
+    bps = (max_blocks + S - 1) / S;
+  }
+  const int beg = s * bps;
+  const int end = min(n, beg + bps);
+  const int cnt = end > beg ? end - beg : 0;
+  const int per = (cnt + kDecodeWaves - 1) / kDecodeWaves;
+  const int wb = beg + wave * per;
+  const int we = min(end, wb + per);
+
+  typename F::Q qf;
+  F::load_q(qf, q + ((size_t)r * H + i) * G * D, col, quad, G);
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  floatx4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* sel_row = SPARSE ? sel_idx + ((size_t)r * H + i) * max_sel : nullptr;
+  const int32_t* tab_row = table + (size_t)r * max_blocks;
+  const size_t head_stride = (size_t)kBlock * D;  // elements per (block, head) tile
+
+  for (int g0 = wb; g0 < we; g0 += 64) {
+    const int gn = min(64, we - g0);
+    int my_blk = 0, my_pid = 0;
+    if (lane < gn) {
+      my_blk = SPARSE ? clampi(sel_row[g0 + lane], 0, M - 1) : g0 + lane;
+      my_pid = clampi(tab_row[my_blk], 0, num_pool_blocks - 1);
+    }
+
+    auto load_chunk = [&](Chunk<T, D>& c, int at) {
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        if (at + j < gn) {
+          const int b = __builtin_amdgcn_readlane(my_blk, at + j);
+          const int p = __builtin_amdgcn_readlane(my_pid, at + j);
+          const size_t tile = ((size_t)p * H + i) * head_stride;
+          F::load_kv(c.f[j], k_pool + tile, v_pool + tile, col, quad);
+          c.blk[j] = b;
+        } else {
+          c.blk[j] = -1;
+        }
+      }
+    };
+
+    auto compute_chunk = [&](Chunk<T, D>& c) {
+      floatx4_t sv[kChunk];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        if (c.blk[j] >= 0) {
+          sv[j] = F::qk(c.f[j], qf);
+          const int tok0 = c.blk[j] * kBlock + 4 * quad;
+          const bool partial = c.blk[j] * kBlock + kBlock > L;
+          unsigned keep = 0xfu;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool ok = !partial || tok0 + e < L;
+            sv[j][e] = ok ? sv[j][e] * scale_log2 : -INFINITY;
+            keep &= ok ? 0xfu : ~(1u << e);
+            mx = fmaxf(mx, sv[j][e]);
+          }
+          if (partial) F::mask_v(c.f[j], keep);
+        } else {
+          sv[j] = floatx4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      // With nothing valid seen yet (m_new = -inf) keep the state unchanged;
+      // otherwise alpha = 0 on the first chunk (m_run = -inf).
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m_run - m_use);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        if (c.blk[j] >= 0) {
+          float p[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = exp2f(sv[j][e] - m_use);
+            l_run += p[e];
+          }
+          F::pv(acc, c.f[j], p);
+        }
+      }
+    };
+
+    Chunk<T, D> cur;
+    load_chunk(cur, 0);
+    for (int at = 0; at < gn; at += kChunk) {
+      Chunk<T, D> nxt;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) nxt.blk[j] = -1;
+      if (at + kChunk < gn) load_chunk(nxt, at + kChunk);
+      compute_chunk(cur);
+      cur = nxt;
+    }
+  }
+
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    *reinterpret_cast<floatx4_t*>(&s_acc[wave][col][16 * t + 4 * quad]) = acc[t];
+  if (quad == 0) {
+    s_m[wave][col] = m_run;
+    s_l[wave][col] = l_run;
+  }
+  __syncthreads();
+
+  const size_t prow = ((size_t)r * H + i) * S + s;  // partial row of this workgroup
+  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
+    const int j = idx / D;
+    const int c = idx % D;
+    float mw = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) mw = fmaxf(mw, s_m[w][j]);
+    float o = 0.f, l = 0.f;
+    if (mw != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const float wt = exp2f(s_m[w][j] - mw);
+        o += wt * s_acc[w][j][c];
+        l += wt * s_l[w][j];
+      }
+    }
+    part_o[(prow * G + j) * D + c] = o;
+    if (c == 0) {
+      part_ml[(prow * G + j) * 2] = mw;
+      part_ml[(prow * G + j) * 2 + 1] = l;
+    }
+  }
+}
+
+// out[r][h][c] = sum_s 2^(m_s - m) o_s[c] / sum_s 2^(m_s - m) l_s.
+__global__ void merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                             float* __restrict__ out, int H, int G, int D, int S, int rows_per_head,
+                             int row_stride_out) {
+  // blockIdx.x = query row within (r, i); blockIdx.y = i; blockIdx.z = r
+  const int row = blockIdx.x;
+  const int i = blockIdx.y;
+  const int r = blockIdx.z;
+  const size_t base = ((size_t)r * H + i) * S;  // first partial row (times rows_per_head)
+  float m = -INFINITY;
+  for (int s = 0; s < S; ++s) m = fmaxf(m, part_ml[((base + s) * rows_per_head + row) * 2]);
+  const int j = row % G;
+  const int t = row / G;
+  float* dst = out + (((size_t)r * row_stride_out + t) * H * G + (size_t)i * G + j) * D;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    if (m != -INFINITY) {
+      for (int s = 0; s < S; ++s) {
+        const size_t pr = (base + s) * rows_per_head + row;
+        const float wt = exp2f(part_ml[pr * 2] - m);
+        num += wt * part_o[pr * D + c];
+        den += wt * part_ml[pr * 2 + 1];
+      }
+    }
+    dst[c] = den > 0.f ? num / den : 0.f;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)a.splits, (unsigned)a.H, (unsigned)a.R);
+  if (a.sel_idx) {
+    hipLaunchKernelGGL((decode_kernel<T, D, true>), grid, dim3(kDecodeThreads), 0, stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
+                       static_cast<const T*>(a.v_pool), a.table, a.seq_lens, a.sel_idx, a.sel_cnt, a.max_sel,
+                       a.part_o, a.part_ml, a.H, a.G, a.max_blocks, a.num_pool_blocks, a.splits, a.scale_log2);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<T, D, false>), grid, dim3(kDecodeThreads), 0, stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
+                       static_cast<const T*>(a.v_pool), a.table, a.seq_lens, nullptr, nullptr, 0, a.part_o,
+                       a.part_ml, a.H, a.G, a.max_blocks, a.num_pool_blocks, a.splits, a.scale_log2);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)a.G, (unsigned)a.H, (unsigned)a.R), dim3(a.D), 0, stream,
+                     a.part_o, a.part_ml, a.out, a.H, a.G, a.D, a.splits, a.G, 1);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(const float* part_o, const float* part_ml, float* out, int R, int H, int G, int D, int S,
+                        int rows_per_head, int row_stride_out, hipStream_t stream) {
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows_per_head, (unsigned)H, (unsigned)R), dim3(D), 0, stream,
+                     part_o, part_ml, out, H, G, D, S, rows_per_head, row_stride_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.dtype == 0)
+    return a.D == 128 ? launch_decode_t<bf16_t, 128>(a, stream) : launch_decode_t<bf16_t, 64>(a, stream);
+  return a.D == 128 ? launch_decode_t<float, 128>(a, stream) : launch_decode_t<float, 64>(a, stream);
+}
+
+}  // namespace resa

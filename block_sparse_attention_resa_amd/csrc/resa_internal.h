@@ -1,0 +1,130 @@
+// Internal declarations shared by the libresa translation units: device
+// helpers (bf16 handling, order-preserving keys, MFMA operand types) and the
+// host-side launchers each kernel file exports to the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace resa {
+
+constexpr int kBlock = 16;  // tokens per KV block
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) short short4_t;
+typedef __attribute__((ext_vector_type(4))) float floatx4_t;
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+// ----------------------------------------------------------------- scalars
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+__device__ __forceinline__ float bf16_lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Order-preserving maps to unsigned integers: a < b as floats (with -0 < +0)
+// iff key(a) < key(b) as unsigned integers.
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t u32_order_key(uint32_t u) {
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t u32_from_order_key(uint32_t k) {
+  return (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+}
+__device__ __forceinline__ uint32_t bf16_order_key(uint32_t h) {  // h: 16-bit pattern
+  return (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
+}
+__device__ __forceinline__ uint32_t bf16_from_order_key(uint32_t k) {
+  return (k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu);
+}
+
+// ----------------------------------------------------------------- launchers
+// Each launcher enqueues on `stream` and returns hipGetLastError()'s result.
+
+struct DescArgs {
+  const void* k_pool;
+  void* desc_pool;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  const int32_t* first_block;  // nullable
+  int32_t num_blocks;          // range selector, see resa_build_descriptors
+  int32_t window;              // > 0: blocks floor((L-window)/16) .. M-1 (rectify)
+  int32_t R, H, D, dtype, max_blocks, num_pool_blocks;
+};
+hipError_t launch_descriptors(const DescArgs& a, hipStream_t stream);
+
+struct ScoreArgs {
+  const void* q;
+  const void* desc_pool;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  uint32_t* keys;  // [R][H][max_blocks] workspace
+  float* scores;   // nullable export [R][H][max_blocks]
+  int32_t R, H, G, D, dtype, max_blocks, num_pool_blocks, mode;
+};
+hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream);
+
+struct SelectArgs {
+  const uint32_t* keys;
+  const int32_t* seq_lens;
+  int32_t* sel_idx;
+  int32_t* sel_cnt;
+  int32_t R, H, max_blocks, max_sel;
+  int32_t budget_num, budget_den, min_blocks, local_blocks;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  const int32_t* sel_idx;  // null for dense
+  const int32_t* sel_cnt;  // null for dense
+  int32_t max_sel;
+  float* out;
+  float* part_o;   // [R][H][S][G][D]
+  float* part_ml;  // [R][H][S][G][2]
+  int32_t R, H, G, D, dtype, max_blocks, num_pool_blocks, splits;
+  float scale_log2;  // sm_scale * log2(e)
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Log-sum-exp merge of split partials: out row (r, t, i*G + j) from
+// part_o / part_ml rows ((r*H + i)*S + s)*rows_per_head + t*G + j.
+hipError_t launch_merge(const float* part_o, const float* part_ml, float* out, int R, int H, int G, int D, int S,
+                        int rows_per_head, int row_stride_out, hipStream_t stream);
+
+struct RectifyArgs {
+  const void* q_chunk;
+  const void* k_new;
+  const void* v_new;
+  void* k_pool;
+  void* v_pool;
+  void* desc_pool;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  float* out;
+  float* part_o;   // [R][H][S][chunk*G][D]
+  float* part_ml;  // [R][H][S][chunk*G][2]
+  int32_t R, H, G, D, dtype, max_blocks, num_pool_blocks, chunk, splits;
+  float scale_log2;
+};
+hipError_t launch_rectify(const RectifyArgs& a, hipStream_t stream);
+
+}  // namespace resa

@@ -198,8 +198,9 @@ def make_layer(spec: WorkloadSpec, seed: int, layer: int = 0, device="cpu",
             blocks = sorted(torch.randperm(max(M - 1, 1), generator=small)[:cnt].tolist()) if cnt else []
             if blocks:
                 qbar = qf[r, i * g:(i + 1) * g].mean(dim=0)
-                rows = torch.cat([torch.arange(b * BLOCK, min(b * BLOCK + BLOCK, L), device=device)
-                                  for b in blocks])
+                bt = torch.tensor(blocks, device=device, dtype=torch.int64)
+                rows = (bt[:, None] * BLOCK + torch.arange(BLOCK, device=device)[None, :]).flatten()
+                rows = rows[rows < L]
                 z[i][rows] += spec.plant_alpha * qbar
             plant_r.append(blocks)
         planted.append(plant_r)
