@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Benchmark of the ReSA decode hot path on one MI355X.
+
+Workload (default): one request at 262144 tokens of context through a stack
+of 28 independent Qwen2.5-7B-shaped attention layers (28 query heads over 4
+KV heads, head dim 128, bf16, block 16, 10% block budget = 1639 of 16384
+blocks per KV head).  Inputs are seeded synthetic data (see synth/).
+
+A step is one decoded token through all 28 layers; per layer it runs the
+whole sparse path: tail-descriptor refresh (resa_build_descriptors on the
+last block), resa_score_select and resa_sparse_decode.  The 28-layer step is
+captured once into a HIP graph and replayed, so the timing holds GPU work
+only (the pages measure kernel time without CPU overhead, §5).  Reported:
+
+* value: microseconds per layer-step (lower is better);
+* achieved HBM GB/s of the layer-step on its algorithmic bytes;
+* the build's own dense decode (resa_dense_decode) at the same shape;
+* the rectification call (window 32) at the same shape;
+* roofline of the dominant kernel (sparse decode) from HIP events;
+* the CPU oracle timed on a bounded sample of the same step.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-decode attention µs/layer-step & achieved HBM GB/s at 256K ctx"
+PEAK_HBM_GBPS = 8000.0
+SEED = 2024
+RECT_CHUNK = 32
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(spec, L, n_sel, e):
+    """Bytes the method must move per layer-step (descriptors, selected K/V
+    rows, q, fp32 output), per Eq 6's accounting with a 10% attended fraction."""
+    H, g, d = spec.num_kv_heads, spec.group_size, spec.head_dim
+    M = (L + 15) // 16
+    tail_rows = L - (M - 1) * 16
+    desc = H * M * 2 * d * e
+    kv = H * ((n_sel - 1) * 16 + tail_rows) * 2 * d * e
+    q = H * g * d * e
+    out = H * g * d * 4
+    return {"desc": desc, "kv": kv, "q": q, "out": out, "total": desc + kv + q + out}
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_sparse_attention_resa_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_hash):
+    """HBM bytes per launch of the sparse decode kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "sparse_decode_traffic_256k.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen7b_ctx256k_l28")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg (for profiler runs)")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (HBM counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_resa_amd as resa
+    from synth import WORKLOADS, make_layer, make_paged
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    resa.load_library()
+    torch.cuda.set_device(0)
+    spec = WORKLOADS[args.workload]
+    assert spec.num_requests == 1 and spec.dtype == "bf16"
+    L = spec.seq_lens[0]
+    H, g, d = spec.num_kv_heads, spec.group_size, spec.head_dim
+    e = 2
+    cfg = resa.Config(num_kv_heads=H, group_size=g, head_dim=d, dtype=resa.RESA_BF16)
+    nlayers = spec.layers
+
+    # ---------------------------------------------------------------- setup
+    t_setup = time.perf_counter()
+    layers = []
+    keep0 = None
+    for l in range(nlayers):
+        inp = make_layer(spec, seed=SEED, layer=l, device="cuda")
+        pg = make_paged(inp)
+        if l == 0 and not args.no_cpu_baseline:
+            keep0 = (inp.q.cpu(), [k.cpu() for k in inp.keys], [v.cpu() for v in inp.values])
+        kv = resa.PagedKV(pg.k_pool, pg.v_pool, pg.desc_pool, pg.block_table, pg.seq_lens)
+        resa.build_descriptors(cfg, kv)
+        layers.append({"kv": kv, "q": inp.q})
+        del inp
+        if (l + 1) % 7 == 0:
+            torch.cuda.synchronize()
+            log(f"layer {l + 1}/{nlayers} generated")
+    mb = layers[0]["kv"].max_blocks
+    ms = resa.selection_count(cfg, mb)
+    n_sel = resa.selection_count(cfg, (L + 15) // 16)
+    for st in layers:
+        st["sel_idx"] = torch.empty((1, H, ms), dtype=torch.int32, device="cuda")
+        st["sel_cnt"] = torch.empty((1, H), dtype=torch.int32, device="cuda")
+        st["out"] = torch.empty((1, H * g, d), dtype=torch.float32, device="cuda")
+        st["out_dense"] = torch.empty((1, H * g, d), dtype=torch.float32, device="cuda")
+    ws_sel = resa.alloc_workspace(cfg, resa.OP_SCORE_SELECT, 1, mb, ms)
+    ws_dec = resa.alloc_workspace(cfg, resa.OP_SPARSE_DECODE, 1, mb, ms)
+    ws_den = resa.alloc_workspace(cfg, resa.OP_DENSE_DECODE, 1, mb)
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f}s, {nlayers} layers, "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB resident")
+
+    def tail_refresh(st):
+        resa.build_descriptors(cfg, st["kv"], None, 1)
+
+    def score_select(st):
+        resa.score_select(cfg, st["kv"], st["q"], st["sel_idx"], st["sel_cnt"], ws_sel)
+
+    def sparse_decode(st):
+        resa.sparse_decode(cfg, st["kv"], st["q"], st["sel_idx"], st["sel_cnt"], st["out"], ws_dec)
+
+    def dense_decode(st):
+        resa.dense_decode(cfg, st["kv"], st["q"], st["out_dense"], ws_den)
+
+    def sparse_step():
+        for st in layers:
+            tail_refresh(st)
+            score_select(st)
+            sparse_decode(st)
+
+    def dense_step():
+        for st in layers:
+            dense_decode(st)
+
+    def capture(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        torch.cuda.synchronize()
+        return graph
+
+    def time_graph(graph, steps, warmup):
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - w0) * 1e3 / steps
+        return wall, e0.elapsed_time(e1) / steps
+
+    def time_calls(fn, reps=1):
+        """Average GPU duration of one call (HIP events bracketing the call on
+        torch's stream; a preceding GPU sleep keeps the launches queued, so the
+        interval holds the call's kernels only)."""
+        pairs = []
+        for _ in range(reps):
+            for st in layers:
+                torch.cuda._sleep(200_000)
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn(st)
+                b.record()
+                pairs.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3  # us
+
+    # ---------------------------------------------------------------- sparse step
+    g_sparse = capture(sparse_step)
+    log("captured sparse step graph")
+    wall_ms, ev_ms = time_graph(g_sparse, args.steps, args.warmup)
+    us_layer = wall_ms * 1e3 / nlayers
+    log(f"sparse: {wall_ms:.3f} ms/step (events {ev_ms:.3f}), {us_layer:.2f} us/layer-step")
+
+    # per-call breakdown (eager, queued behind a GPU sleep)
+    t_tail = time_calls(tail_refresh)
+    t_sel = time_calls(score_select)
+    t_dec = time_calls(sparse_decode)
+    log(f"breakdown us: tail {t_tail:.2f}  score+select {t_sel:.2f}  sparse decode {t_dec:.2f}")
+
+    # ---------------------------------------------------------------- dense
+    g_dense = capture(dense_step)
+    dwall_ms, dev_ms = time_graph(g_dense, max(5, args.steps // 5), 2)
+    us_dense = dwall_ms * 1e3 / nlayers
+    log(f"dense: {dwall_ms:.3f} ms/step, {us_dense:.2f} us/layer-step")
+    del g_dense
+
+    # ---------------------------------------------------------------- bytes
+    ab = algorithmic_bytes(spec, L, n_sel, e)
+    dense_bytes = H * L * 2 * d * e + ab["q"] + ab["out"]
+    gbps = ab["total"] / (us_layer * 1e-6) / 1e9
+    dec_bytes = ab["kv"] + ab["q"] + ab["out"]
+    dec_gbps = dec_bytes / (t_dec * 1e-6) / 1e9
+    khash = source_hash("decode.hip", "attn_frag.h", "resa_internal.h")
+    traffic = measured_traffic(khash)
+
+    # ---------------------------------------------------------------- check + CPU oracle
+    cpu = None
+    check = None
+    if keep0 is not None:
+        import oracle as O
+        from threadpoolctl import threadpool_limits
+
+        torch.cuda.synchronize()
+        q0, k0, v0 = keep0
+        scale = float(np.float32(1 / math.sqrt(d)))
+        qs = [q0[0, i * g:(i + 1) * g].float().numpy().astype(np.float64) for i in range(H)]
+        Ks = [k0[0][i].float().numpy().astype(np.float64) for i in range(H)]
+        Vs = [v0[0][i].float().numpy().astype(np.float64) for i in range(H)]
+        log("oracle: building the layer-0 block key cache (not timed)")
+        desc = [O.descriptors(Ks[i], L) for i in range(H)]
+        # sanity check of the timed GPU outputs of layer 0 against the oracle on the GPU's selection
+        sel = layers[0]["sel_idx"].cpu()
+        cnt = layers[0]["sel_cnt"].cpu()
+        out0 = layers[0]["out"].cpu().numpy()
+        errs = []
+        for i in range(H):
+            blocks = sel[0, i, : int(cnt[0, i])].tolist()
+            ref = O.attend(qs[i], Ks[i], Vs[i], L, blocks, scale)
+            errs.append(float(np.abs(out0[0, i * g:(i + 1) * g] - ref).max()))
+        check = max(errs)
+        log(f"layer-0 output vs oracle: max abs err {check:.2e}")
+        log("oracle: timing the layer-step on the host")
+        reps = 0
+        t0 = time.perf_counter()
+        with threadpool_limits(limits=1):
+            while reps < 1 or (time.perf_counter() - t0 < 10.0 and reps < 5):
+                for i in range(H):
+                    lo, hi = desc[i]
+                    lo[-1], hi[-1] = O.block_descriptor(Ks[i], L, (L + 15) // 16 - 1)
+                    S = O.scores(qs[i], lo, hi)
+                    blocks = O.select(S)
+                    O.attend(qs[i], Ks[i], Vs[i], L, blocks, scale)
+                reps += 1
+        cpu_us = (time.perf_counter() - t0) / reps * 1e6
+        cpu = {"value": round(cpu_us, 1), "unit": "us/layer-step", "cores": 1, "kind": "oracle",
+               "sample": f"{reps} layer-step(s) of layer 0 (4 KV heads: tail descriptor, 16384 block "
+                         f"scores, top-1639 selection, attention over the selected blocks), NumPy fp64, "
+                         f"1 thread"}
+        log(f"oracle: {cpu_us / 1e3:.1f} ms per layer-step ({reps} reps)")
+        del Ks, Vs, desc
+
+    # ---------------------------------------------------------------- rectification
+    qc = torch.randn((1, RECT_CHUNK, H * g, d), device="cuda").to(torch.bfloat16)
+    kn = torch.randn((1, RECT_CHUNK, H, d), device="cuda").to(torch.bfloat16)
+    vn = torch.randn((1, RECT_CHUNK, H, d), device="cuda").to(torch.bfloat16)
+    rout = torch.empty((1, RECT_CHUNK, H * g, d), device="cuda")
+    ws_rect = resa.alloc_workspace(cfg, resa.OP_DENSE_RECTIFY, 1, mb, chunk=RECT_CHUNK)
+
+    def rectify(st):
+        resa.dense_rectify(cfg, st["kv"], qc, kn, vn, rout, ws_rect)
+
+    t_rect = time_calls(rectify)
+    rect_flops = H * g * sum(4 * d * (L - RECT_CHUNK + t + 1) for t in range(RECT_CHUNK))
+    log(f"rectify (window {RECT_CHUNK}): {t_rect:.1f} us/layer, {rect_flops / (t_rect * 1e-6) / 1e12:.1f} TFLOP/s")
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib * 2**20 // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    line = {
+        "metric": METRIC,
+        "value": round(us_layer, 3),
+        "unit": "us/layer-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "requests": 1, "ctx": L, "layers": nlayers, "q_heads": H * g,
+                   "kv_heads": H, "head_dim": d, "block": 16, "budget": "1/10", "selected_blocks": n_sel,
+                   "step": "28 layers x (tail descriptor + score/select + sparse decode), HIP graph"},
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes_per_layer_step": ab["total"],
+        "tokens_per_s": round(1e3 / wall_ms, 1),
+        "dense_us_per_layer_step": round(us_dense, 3),
+        "speedup_vs_dense": round(us_dense / us_layer, 3),
+        "dense_hbm_gbps": round(dense_bytes / (us_dense * 1e-6) / 1e9, 1),
+        "breakdown_us": {"tail_descriptor": round(t_tail, 2), "score_select": round(t_sel, 2),
+                         "sparse_decode": round(t_dec, 2)},
+        "rectify_us_per_layer": round(t_rect, 1),
+        "rectify_window": RECT_CHUNK,
+        "rectify_tflops": round(rect_flops / (t_rect * 1e-6) / 1e12, 2),
+        "roofline": {"bound": "hbm", "kernel": "sparse decode (resa_sparse_decode)",
+                     "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "bytes_per_launch": dec_bytes, "avg_launch_us": round(t_dec, 3),
+                     "kernel_source_hash": khash},
+        "cpu_baseline": cpu,
+        "oracle_check_max_abs_err": check,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -82,12 +82,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     n = M;
     bps = (max_blocks + S - 1) / S;
   }
+  // The split and wavefront ranges depend only on the list capacity, so the
+  // block-id loads below do not wait for sel_cnt; n only trims the range.
   const int beg = s * bps;
-  const int end = min(n, beg + bps);
-  const int cnt = end > beg ? end - beg : 0;
-  const int per = (cnt + kDecodeWaves - 1) / kDecodeWaves;
+  const int per = (bps + kDecodeWaves - 1) / kDecodeWaves;
+  const int cap = SPARSE ? max_sel : max_blocks;
   const int wb = beg + wave * per;
-  const int we = min(end, wb + per);
+  const int we_cap = min(min(beg + bps, cap), wb + per);  // positions readable without n
+  const int we = min(we_cap, n);
 
   typename F::Q qf;
   F::load_q(qf, q + ((size_t)r * H + i) * G * D, col, quad, G);
@@ -102,13 +104,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const int32_t* tab_row = table + (size_t)r * max_blocks;
   const size_t head_stride = (size_t)kBlock * D;  // elements per (block, head) tile
 
-  for (int g0 = wb; g0 < we; g0 += 64) {
-    const int gn = min(64, we - g0);
+  for (int g0 = wb; g0 < we_cap; g0 += 64) {
+    // Ids and physical blocks of up to 64 positions, fetched before n and L
+    // are known (every address stays inside the list and the table); a block
+    // id past the sequence end only contributes masked rows.
     int my_blk = 0, my_pid = 0;
-    if (lane < gn) {
-      my_blk = SPARSE ? clampi(sel_row[g0 + lane], 0, M - 1) : g0 + lane;
+    if (g0 + lane < we_cap) {
+      my_blk = SPARSE ? clampi(sel_row[g0 + lane], 0, max_blocks - 1) : g0 + lane;
       my_pid = clampi(tab_row[my_blk], 0, num_pool_blocks - 1);
     }
+    if (g0 >= we) break;
+    const int gn = min(64, we - g0);
 
     auto load_chunk = [&](Chunk<T, D>& c, int at) {
 #pragma unroll
@@ -219,31 +225,94 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   }
 }
 
-// out[r][h][c] = sum_s 2^(m_s - m) o_s[c] / sum_s 2^(m_s - m) l_s.
-__global__ void merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                             float* __restrict__ out, int H, int G, int D, int S, int rows_per_head,
-                             int row_stride_out) {
-  // blockIdx.x = query row within (r, i); blockIdx.y = i; blockIdx.z = r
+// Log-sum-exp merge of split partials.  One workgroup per output row:
+//   out[c] = sum_s 2^(m_s - m) o_s[c] / sum_s 2^(m_s - m) l_s,  m = max_s m_s.
+// The split weights are computed once into LDS; the weighted sum is spread
+// over (channel quad, split subset) pairs so every thread issues a batch of
+// independent 16-byte loads, then reduced through LDS.
+constexpr int kMergeThreads = 256;
+
+__device__ __forceinline__ float block_reduce(float v, float* lds, bool is_max) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float o = __shfl_xor(v, off);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  float r = lds[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) r = is_max ? fmaxf(r, lds[w]) : r + lds[w];
+  __syncthreads();
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part_o,
+                                                              const float* __restrict__ part_ml,
+                                                              float* __restrict__ out, int H, int G, int S,
+                                                              int rows_per_head, int row_stride_out) {
+  constexpr int C4 = D / 4;                  // float4 lanes per row
+  constexpr int NG = kMergeThreads / C4;     // split subsets
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[kMergeThreads / 64];
+  __shared__ floatx4_t s_acc[kMergeThreads];
   const int row = blockIdx.x;
   const int i = blockIdx.y;
   const int r = blockIdx.z;
-  const size_t base = ((size_t)r * H + i) * S;  // first partial row (times rows_per_head)
+  const int tid = threadIdx.x;
+  const size_t base = ((size_t)r * H + i) * S;
+
   float m = -INFINITY;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, part_ml[((base + s) * rows_per_head + row) * 2]);
-  const int j = row % G;
-  const int t = row / G;
-  float* dst = out + (((size_t)r * row_stride_out + t) * H * G + (size_t)i * G + j) * D;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    if (m != -INFINITY) {
-      for (int s = 0; s < S; ++s) {
-        const size_t pr = (base + s) * rows_per_head + row;
-        const float wt = exp2f(part_ml[pr * 2] - m);
-        num += wt * part_o[pr * D + c];
-        den += wt * part_ml[pr * 2 + 1];
-      }
+  float lv[kMaxSplits / kMergeThreads];
+#pragma unroll
+  for (int k = 0; k < kMaxSplits / kMergeThreads; ++k) {
+    const int s = tid + k * kMergeThreads;
+    lv[k] = 0.f;
+    if (s < S) {
+      const size_t pr = (base + s) * rows_per_head + row;
+      const float ms = part_ml[pr * 2];
+      lv[k] = part_ml[pr * 2 + 1];
+      s_w[s] = ms;
+      m = fmaxf(m, ms);
     }
-    dst[c] = den > 0.f ? num / den : 0.f;
+  }
+  m = block_reduce(m, s_red, true);
+  float den = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxSplits / kMergeThreads; ++k) {
+    const int s = tid + k * kMergeThreads;
+    if (s < S) {
+      const float ms = s_w[s];
+      const float w = (m == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - m);
+      s_w[s] = w;
+      den += w * lv[k];
+    }
+  }
+  den = block_reduce(den, s_red, false);  // its barriers also publish s_w
+
+  const int c4 = tid % C4;
+  const int grp = tid / C4;
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = grp; s < S; s += NG) {
+    const float w = s_w[s];
+    const floatx4_t o = *reinterpret_cast<const floatx4_t*>(part_o + ((base + s) * rows_per_head + row) * D + 4 * c4);
+    acc += w * o;
+  }
+  s_acc[tid] = acc;
+  __syncthreads();
+  if (grp == 0) {
+    floatx4_t sum = acc;
+#pragma unroll
+    for (int gi = 1; gi < NG; ++gi) sum += s_acc[gi * C4 + c4];
+    const int j = row % G;
+    const int t = row / G;
+    float* dst = out + (((size_t)r * row_stride_out + t) * H * G + (size_t)i * G + j) * D + 4 * c4;
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    *reinterpret_cast<floatx4_t*>(dst) = sum * inv;
   }
 }
 
@@ -263,17 +332,20 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)a.G, (unsigned)a.H, (unsigned)a.R), dim3(a.D), 0, stream,
-                     a.part_o, a.part_ml, a.out, a.H, a.G, a.D, a.splits, a.G, 1);
-  return hipGetLastError();
+  return launch_merge(a.part_o, a.part_ml, a.out, a.R, a.H, a.G, a.D, a.splits, a.G, 1, stream);
 }
 
 }  // namespace
 
 hipError_t launch_merge(const float* part_o, const float* part_ml, float* out, int R, int H, int G, int D, int S,
                         int rows_per_head, int row_stride_out, hipStream_t stream) {
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows_per_head, (unsigned)H, (unsigned)R), dim3(D), 0, stream,
-                     part_o, part_ml, out, H, G, D, S, rows_per_head, row_stride_out);
+  const dim3 grid((unsigned)rows_per_head, (unsigned)H, (unsigned)R);
+  if (D == 128)
+    hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(kMergeThreads), 0, stream, part_o, part_ml, out, H, G, S,
+                       rows_per_head, row_stride_out);
+  else
+    hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(kMergeThreads), 0, stream, part_o, part_ml, out, H, G, S,
+                       rows_per_head, row_stride_out);
   return hipGetLastError();
 }
 

@@ -96,7 +96,7 @@ int splits_for(const resa_config* c, int op, int R, int max_blocks, int max_sel,
   }
   if (s > len) s = len;
   if (s < 1) s = 1;
-  if (s > 65535) s = 65535;
+  if (s > kMaxSplits) s = kMaxSplits;
   return (int)s;
 }
 

@@ -9,7 +9,8 @@
 
 namespace resa {
 
-constexpr int kBlock = 16;  // tokens per KV block
+constexpr int kBlock = 16;       // tokens per KV block
+constexpr int kMaxSplits = 1024;  // split partials one merge workgroup combines
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) short short4_t;

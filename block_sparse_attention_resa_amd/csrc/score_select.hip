@@ -17,14 +17,15 @@
 // the coefficients stay in registers.  Scores are written as order-preserving
 // 32-bit keys for the selection kernel.
 //
-// Selection.  One 1024-thread workgroup per (request, KV head).  Thread t
-// owns a contiguous run of candidate blocks, held in registers.  The
-// (n - n_local)-th largest key among the older blocks is found by an MSB-first
-// radix select over the bits in which the candidates differ, with a 256-bin
-// LDS histogram per 8-bit digit; the pass stops early once every key of the
-// boundary bucket is needed.  Blocks above the threshold are taken, blocks
-// equal to it are taken lowest index first, and a block-wide prefix count
-// writes the selected ids in ascending order.
+// Selection.  One 1024-thread workgroup per (request, KV head); thread t
+// owns candidate blocks t, t + 1024, ... (coalesced loads, kept in
+// registers).  The (n - n_local)-th largest key among the older blocks is
+// found MSB-first over the bits in which the candidates differ: 11-bit
+// histogram passes in LDS narrow the boundary bucket to at most 256 keys, then
+// one wavefront resolves the remaining bits with ballot counts.  Blocks above
+// the threshold are taken, blocks equal to it lowest index first, and one
+// scanned table of per-(round, wavefront) ballot counts places every selected
+// id in ascending order.
 #include "resa_internal.h"
 
 namespace resa {
@@ -38,6 +39,11 @@ struct ChunkLoad;
 template <>
 struct ChunkLoad<bf16_t> {
   static constexpr int kVals = 16;  // bf16 values per 32-byte chunk
+  using Pair = uint32_t;            // two consecutive channels
+  __device__ static void unpack_pair(uint32_t w, float& a, float& b) {
+    a = bf16_lo_f32(w);
+    b = bf16_hi_f32(w);
+  }
   __device__ static void unpack(const uint4& a, const uint4& b, float* f) {
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -46,12 +52,16 @@ struct ChunkLoad<bf16_t> {
       f[2 * e + 1] = bf16_hi_f32(w[e]);
     }
   }
-  __device__ static float load_q(const bf16_t* p) { return __uint_as_float((uint32_t)p->bits << 16); }
 };
 
 template <>
 struct ChunkLoad<float> {
   static constexpr int kVals = 8;
+  using Pair = uint2;
+  __device__ static void unpack_pair(uint2 w, float& a, float& b) {
+    a = __uint_as_float(w.x);
+    b = __uint_as_float(w.y);
+  }
   __device__ static void unpack(const uint4& a, const uint4& b, float* f) {
     f[0] = __uint_as_float(a.x);
     f[1] = __uint_as_float(a.y);
@@ -62,25 +72,25 @@ struct ChunkLoad<float> {
     f[6] = __uint_as_float(b.z);
     f[7] = __uint_as_float(b.w);
   }
-  __device__ static float load_q(const float* p) { return *p; }
 };
 
 constexpr int kScoreUnroll = 4;
 
-template <typename T, int D>
+template <typename T, int D, int MODE, int MAXG>
 __global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, const T* __restrict__ desc,
                                                     const int32_t* __restrict__ table,
                                                     const int32_t* __restrict__ seq_lens,
                                                     uint32_t* __restrict__ keys, float* __restrict__ scores, int H,
-                                                    int G, int max_blocks, int num_pool_blocks, int mode,
-                                                    int blocks_per_wg) {
+                                                    int G, int max_blocks, int num_pool_blocks) {
   using CL = ChunkLoad<T>;
   constexpr int VPL = CL::kVals;
   constexpr int CH = 2 * D / VPL;  // lanes per descriptor
   constexpr int HALF = CH / 2;     // lanes per descriptor row
+  extern __shared__ float s_coef[];  // [H][2][D]: N (min row) then P (max row)
 
   const int r = blockIdx.y;
   const int t = threadIdx.x;
+  const int lane = t & 63;
   const int grp = t / CH;
   const int lg = t % CH;
   const int part = lg / HALF;  // 0: min row, 1: max row
@@ -88,72 +98,118 @@ __global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, co
   const int head = grp % H;
   const int bsub = grp / H;
   const int bpi = blockDim.x / (CH * H);  // blocks per iteration
+  const int wg_blocks = bpi * kScoreUnroll;
+  const int wg_b0 = blockIdx.x * wg_blocks;
+  uint32_t* key_row = keys + ((size_t)r * H + head) * max_blocks;
+  float* score_row = scores ? scores + ((size_t)r * H + head) * max_blocks : nullptr;
 
-  // Fold the group's queries into this thread's slice of P (max row) or N (min row).
-  float coef[VPL];
+  // Physical ids of this workgroup's blocks: one coalesced load per wavefront
+  // (all table columns are in bounds), handed to the lanes with a shuffle.
+  // Blocks past the sequence end are dropped at the end, so no address here
+  // waits for seq_lens.
+  int my_pid = 0;
+  if (lane < wg_blocks && wg_b0 + lane < max_blocks) my_pid = table[(size_t)r * max_blocks + wg_b0 + lane];
+  // Load order matters: the in-order vector-memory counter makes a wait for
+  // a load also wait for every load issued before it.  The table entries
+  // (needed for the descriptor addresses) go out first, then the group's
+  // query values, then the descriptor loads.  Every thread folds channel pairs of the
+  // queries into P = sum_j max(q_j, 0) and N = sum_j min(q_j, 0) (MODE 0) or
+  // the positive / negative part of the mean query (MODE 1); all G rows are
+  // loaded before any is used (rows past G re-read row G-1 and are ignored).
+  constexpr int kMaxG = MAXG;
+  using Pair = typename CL::Pair;
+  const int npairs = H * D / 2;
+  const int nthr = blockDim.x;
+  // This thread's first channel pair is loaded here; further pairs (only when
+  // H*D/2 exceeds the workgroup size) are folded after the descriptor loads.
+  Pair qv[kMaxG];
   {
-    const T* qh = q + ((size_t)r * H * G + (size_t)head * G) * D + c0;
+    // branch-free (a thread past the last pair re-reads it), so no wait is
+    // placed at a join before the descriptor loads
+    const int v0 = t < npairs ? t : npairs - 1;
+    const T* qh = q + ((size_t)r * H * G + (size_t)(v0 / (D / 2)) * G) * D + (v0 % (D / 2)) * 2;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) coef[v] = 0.f;
-    if (mode == 0) {
-      for (int j = 0; j < G; ++j) {
+    for (int j = 0; j < kMaxG; ++j) qv[j] = *reinterpret_cast<const Pair*>(qh + (size_t)min(j, G - 1) * D);
+  }
+  uint4 buf[kScoreUnroll][2];
+  int bl[kScoreUnroll];
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          const float x = CL::load_q(qh + (size_t)j * D + v);
-          coef[v] += part ? fmaxf(x, 0.f) : fminf(x, 0.f);
-        }
-      }
+  for (int u = 0; u < kScoreUnroll; ++u) {
+    const int bo = u * bpi + bsub;
+    const int b = wg_b0 + bo;
+    bl[u] = b;
+    const int p = clampi(__shfl(my_pid, bo), 0, num_pool_blocks - 1);
+    if (b < max_blocks) {
+      const uint4* src = reinterpret_cast<const uint4*>(desc + (((size_t)p * H + head) * 2 + part) * D + c0);
+      buf[u][0] = src[0];
+      buf[u][1] = src[1];
     } else {
-      for (int j = 0; j < G; ++j) {
+      buf[u][0] = make_uint4(0, 0, 0, 0);
+      buf[u][1] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  for (int v = t; v < npairs; v += nthr) {
+    const int hh = v / (D / 2);
+    const int c = (v % (D / 2)) * 2;
+    if (v != t) {  // rare: more channel pairs than threads
+      const T* qh = q + ((size_t)r * H * G + (size_t)hh * G) * D + c;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) coef[v] += CL::load_q(qh + (size_t)j * D + v);
-      }
+      for (int j = 0; j < kMaxG; ++j) qv[j] = *reinterpret_cast<const Pair*>(qh + (size_t)min(j, G - 1) * D);
+    }
+    float p0 = 0.f, p1 = 0.f, n0 = 0.f, n1 = 0.f;
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const float m = coef[v] / (float)G;
-        coef[v] = part ? fmaxf(m, 0.f) : fminf(m, 0.f);
+    for (int j = 0; j < kMaxG; ++j) {
+      float x0, x1;
+      CL::unpack_pair(qv[j], x0, x1);
+      x0 = j < G ? x0 : 0.f;
+      x1 = j < G ? x1 : 0.f;
+      if constexpr (MODE == 0) {
+        p0 += fmaxf(x0, 0.f);
+        p1 += fmaxf(x1, 0.f);
+        n0 += fminf(x0, 0.f);
+        n1 += fminf(x1, 0.f);
+      } else {
+        p0 += x0;
+        p1 += x1;
       }
     }
+    if constexpr (MODE != 0) {
+      const float m0 = p0 / (float)G, m1 = p1 / (float)G;
+      p0 = fmaxf(m0, 0.f);
+      p1 = fmaxf(m1, 0.f);
+      n0 = fminf(m0, 0.f);
+      n1 = fminf(m1, 0.f);
+    }
+    s_coef[(hh * 2 + 0) * D + c] = n0;
+    s_coef[(hh * 2 + 0) * D + c + 1] = n1;
+    s_coef[(hh * 2 + 1) * D + c] = p0;
+    s_coef[(hh * 2 + 1) * D + c + 1] = p1;
+  }
+  __syncthreads();
+  float coef[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; v += 4) {
+    const floatx4_t c4 = *reinterpret_cast<const floatx4_t*>(&s_coef[(head * 2 + part) * D + c0 + v]);
+    coef[v] = c4[0];
+    coef[v + 1] = c4[1];
+    coef[v + 2] = c4[2];
+    coef[v + 3] = c4[3];
   }
 
   const int L = clampi(seq_lens[r], 0, max_blocks * kBlock);
   const int M = (L + kBlock - 1) / kBlock;
-  const int wg_b0 = blockIdx.x * blocks_per_wg;
-  const int iters = blocks_per_wg / bpi;
-  uint32_t* key_row = keys + ((size_t)r * H + head) * max_blocks;
-  float* score_row = scores ? scores + ((size_t)r * H + head) * max_blocks : nullptr;
-
-  for (int it0 = 0; it0 < iters; it0 += kScoreUnroll) {
-    uint4 buf[kScoreUnroll][2];
-    int bl[kScoreUnroll];
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const int b = wg_b0 + (it0 + u) * bpi + bsub;
-      bl[u] = b;
-      if (it0 + u < iters && b < M) {
-        const int p = clampi(table[(size_t)r * max_blocks + b], 0, num_pool_blocks - 1);
-        const uint4* src =
-            reinterpret_cast<const uint4*>(desc + (((size_t)p * H + head) * 2 + part) * D + c0);
-        buf[u][0] = src[0];
-        buf[u][1] = src[1];
-      } else {
-        buf[u][0] = make_uint4(0, 0, 0, 0);
-        buf[u][1] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  for (int u = 0; u < kScoreUnroll; ++u) {
+    float vals[VPL];
+    CL::unpack(buf[u][0], buf[u][1], vals);
+    float acc = 0.f;
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      float vals[VPL];
-      CL::unpack(buf[u][0], buf[u][1], vals);
-      float acc = 0.f;
+    for (int v = 0; v < VPL; ++v) acc = fmaf(coef[v], vals[v], acc);
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) acc = fmaf(coef[v], vals[v], acc);
-#pragma unroll
-      for (int off = HALF; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-      if (lg == 0 && it0 + u < iters && bl[u] < M) {
-        key_row[bl[u]] = f32_order_key(acc);
-        if (score_row) score_row[bl[u]] = acc;
-      }
+    for (int off = HALF; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lg == 0 && bl[u] < M) {
+      key_row[bl[u]] = f32_order_key(acc);
+      if (score_row) score_row[bl[u]] = acc;
     }
   }
 }
@@ -165,25 +221,42 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
   const int unit = CH * a.H;  // threads per block of all heads
   int m = 1;
   while ((unit * m) % 64 != 0) ++m;
-  while (unit * m * 2 <= 256) m *= 2;
+  while (unit * m * 2 <= 256 && m * 2 * kScoreUnroll <= 64) m *= 2;
   const int threads = unit * m;  // <= 1024 checked by the caller
   const int bpi = m;
-  const int blocks_per_wg = bpi * kScoreUnroll;
+  const int blocks_per_wg = bpi * kScoreUnroll;  // <= 64: one table entry per lane
   const int wgs = (a.max_blocks + blocks_per_wg - 1) / blocks_per_wg;
+  const size_t lds = (size_t)a.H * 2 * D * sizeof(float);
   dim3 grid((unsigned)wgs, (unsigned)a.R);
-  hipLaunchKernelGGL((score_kernel<T, D>), grid, dim3(threads), 0, stream, static_cast<const T*>(a.q),
-                     static_cast<const T*>(a.desc_pool), a.table, a.seq_lens, a.keys, a.scores, a.H, a.G,
-                     a.max_blocks, a.num_pool_blocks, a.mode, blocks_per_wg);
+#define RESA_SCORE_LAUNCH(MODE, MAXG)                                                                        \
+  hipLaunchKernelGGL((score_kernel<T, D, MODE, MAXG>), grid, dim3(threads), lds, stream,                     \
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.desc_pool), a.table, a.seq_lens, a.keys, \
+                     a.scores, a.H, a.G, a.max_blocks, a.num_pool_blocks)
+  if (a.G <= 8) {
+    if (a.mode == 0) RESA_SCORE_LAUNCH(0, 8);
+    else RESA_SCORE_LAUNCH(1, 8);
+  } else {
+    if (a.mode == 0) RESA_SCORE_LAUNCH(0, 16);
+    else RESA_SCORE_LAUNCH(1, 16);
+  }
+#undef RESA_SCORE_LAUNCH
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ select
 
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kDigitBits = 11;  // histogram pass: 2048 bins
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kFinishMax = 256;  // boundary bucket size the single-wavefront finish takes
 
-// Exclusive prefix sum over the workgroup (thread order); also returns the total.
+__device__ __forceinline__ unsigned lane_prefix(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
+}
+
+// Exclusive prefix sum over the workgroup in thread order; `total` gets the sum.
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   int incl = v;
@@ -197,7 +270,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& 
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int x = lds_waves[w];
     before += w < wave ? x : 0;
     total += x;
@@ -206,17 +279,78 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& 
   return before + incl - v;
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const uint32_t* __restrict__ keys,
-                                                            const int32_t* __restrict__ seq_lens,
-                                                            int32_t* __restrict__ sel_idx,
-                                                            int32_t* __restrict__ sel_cnt, int H, int max_blocks,
-                                                            int max_sel, int budget_num, int budget_den,
-                                                            int min_blocks, int local_blocks) {
-  __shared__ uint32_t hist[256];
-  __shared__ int lds_waves[kSelWaves];
-  __shared__ uint32_t lds_and[kSelWaves], lds_or[kSelWaves];
-  __shared__ int bc[3];
+// In-place exclusive prefix sum of tab[0, n), n <= 512, by one wavefront:
+// lane l owns entries [l*per, (l+1)*per).
+__device__ __forceinline__ void wave_scan_table(int* tab, int n) {
+  const int lane = threadIdx.x & 63;
+  const int per = (n + 63) / 64;
+  int v[8];
+  int sum = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int idx = lane * per + e;
+    v[e] = (e < per && idx < n) ? tab[idx] : 0;
+    sum += v[e];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int x = __shfl_up(incl, off);
+    if (lane >= off) incl += x;
+  }
+  int run = incl - sum;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int idx = lane * per + e;
+    if (e < per && idx < n) tab[idx] = run;
+    run += v[e];
+  }
+}
+
+// Candidate keys of one (request, KV head).  Thread t owns blocks t + NT*j,
+// so every load instruction of a wavefront reads 256 contiguous bytes.  KPT > 0
+// keeps up to KPT rounds in registers; KPT == 0 re-reads the row (any size).
+template <int NT, int KPT>
+struct KeyRuns {
+  uint32_t reg[KPT > 0 ? KPT : 1];
+  const uint32_t* row;
+  int C, rounds;
+  __device__ void load(const uint32_t* kr, int c) {
+    row = kr;
+    C = c;
+    rounds = (c + NT - 1) / NT;
+    if constexpr (KPT > 0) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int idx = threadIdx.x + j * NT;
+        reg[j] = kr[idx < c ? idx : c - 1];
+      }
+    }
+  }
+  __device__ bool valid(int j) const { return j < rounds && (int)threadIdx.x + j * NT < C; }
+  __device__ uint32_t key(int j) const {
+    if constexpr (KPT > 0) return reg[j];
+    else return row[threadIdx.x + j * NT];
+  }
+  __device__ int nrounds() const { return KPT > 0 ? KPT : rounds; }
+};
+
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__ keys,
+                                                   const int32_t* __restrict__ seq_lens,
+                                                   int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
+                                                   int H, int max_blocks, int max_sel, int budget_num,
+                                                   int budget_den, int min_blocks, int local_blocks) {
+  constexpr int NW = NT / 64;
+  constexpr int BPT = kBins / NT;                   // histogram bins per thread in the scan
+  constexpr int TAB = KPT > 0 ? NW * KPT : 1;       // per-(round, wavefront) table
+  static_assert(TAB <= 512, "table scan covers at most 512 entries");
+  __shared__ uint32_t hist2[2][kBins];  // alternating pass histograms
+  __shared__ int lds_waves[NW];
+  __shared__ uint32_t lds_and[NW], lds_or[NW];
+  __shared__ uint32_t bucket[kFinishMax];
+  __shared__ int tab[TAB];
+  __shared__ int bc[4];
 
   const int i = blockIdx.x;
   const int r = blockIdx.y;
@@ -229,8 +363,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint32_t* __r
 
   int n = 0, nl = 0;
   if (M > 0) {
-    const long long ceil_part = ((long long)M * budget_num + budget_den - 1) / budget_den;
-    long long nn = ceil_part;
+    long long nn = ((long long)M * budget_num + budget_den - 1) / budget_den;
     if (nn < min_blocks) nn = min_blocks;
     if (nn < local_blocks) nn = local_blocks;
     if (nn > M) nn = M;
@@ -239,50 +372,31 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint32_t* __r
   }
   const int k = n - nl;  // blocks chosen by score
   const int C = M - nl;  // candidates: blocks [0, C)
-  for (int j = tid; j < max_sel; j += kSelThreads) {
+  for (int j = tid; j < max_sel; j += NT) {
     if (j >= n) out[j] = -1;
     else if (j >= k) out[j] = C + (j - k);  // forced recent blocks close the ascending list
   }
   if (tid == 0) sel_cnt[(size_t)r * H + i] = n;
   if (k == 0) return;
   if (k == C) {
-    for (int j = tid; j < C; j += kSelThreads) out[j] = j;
+    for (int j = tid; j < C; j += NT) out[j] = j;
     return;
   }
 
-  const uint32_t* kr = keys + ((size_t)r * H + i) * max_blocks;
-  const int kpt = (C + kSelThreads - 1) / kSelThreads;
-  const int base = tid * kpt;
-  const int cnt = base < C ? (C - base < kpt ? C - base : kpt) : 0;
-
-  uint32_t reg[KPT > 0 ? KPT : 1];
-  auto key_at = [&](int j) -> uint32_t {
-    if constexpr (KPT > 0) {
-      return reg[j];
-    } else {
-      return kr[base + j];
-    }
-  };
-  if constexpr (KPT > 0) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) reg[j] = j < cnt ? kr[base + j] : 0u;
-  }
+  KeyRuns<NT, KPT> kr;
+  kr.load(keys + ((size_t)r * H + i) * max_blocks, C);
+  const int R = kr.nrounds();
+  for (int b = tid; b < kBins; b += NT) hist2[0][b] = 0u;  // published by the next barrier
+  if (tid == 0) bc[3] = 0;
 
   // Bits shared by every candidate key.
   uint32_t a = 0xffffffffu, o = 0u;
-  if constexpr (KPT > 0) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if (j < cnt) {
-        a &= reg[j];
-        o |= reg[j];
-      }
-  } else {
-    for (int j = 0; j < cnt; ++j) {
-      const uint32_t x = kr[base + j];
-      a &= x;
-      o |= x;
-    }
+  for (int j = 0; j < R; ++j) {
+    const bool v = kr.valid(j);
+    const uint32_t x = kr.key(j);
+    a &= v ? x : 0xffffffffu;
+    o |= v ? x : 0u;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -297,7 +411,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint32_t* __r
   a = 0xffffffffu;
   o = 0u;
 #pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     a &= lds_and[w];
     o |= lds_or[w];
   }
@@ -305,92 +419,177 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint32_t* __r
   int top = diff ? 31 - __clz(diff) : -1;  // highest bit in which candidates differ
   uint32_t fixed = top >= 31 ? 0u : (top < 0 ? 0xffffffffu : ~((2u << top) - 1u));
   uint32_t prefix = a & fixed;
-  int remaining = k;  // keys still to take whose fixed bits equal `prefix`
+  int remaining = k;   // keys still to take among those whose fixed bits equal `prefix`
+  int bucket_n = C;    // keys whose fixed bits equal `prefix`
 
-  while (top >= 0) {
-    const int width = top + 1 < 8 ? top + 1 : 8;
+  // Histogram passes over 11-bit digits until the boundary bucket is small.
+  int npass = 0;
+  while (top >= 0 && bucket_n > kFinishMax && remaining != bucket_n) {
+    const int width = top + 1 < kDigitBits ? top + 1 : kDigitBits;
     const int shift = top + 1 - width;
     const uint32_t dmask = (1u << width) - 1u;
-    if (tid < 256) hist[tid] = 0u;
-    __syncthreads();
-    if constexpr (KPT > 0) {
+    uint32_t* hist = hist2[npass & 1];
+    uint32_t* hist_next = hist2[(npass + 1) & 1];
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const uint32_t x = reg[j];
-        if (j < cnt && (x & fixed) == prefix) atomicAdd(&hist[(x >> shift) & dmask], 1u);
+    for (int j = 0; j < R; ++j) {
+      const uint32_t x = kr.key(j);
+      if (kr.valid(j) && (x & fixed) == prefix) atomicAdd(&hist[(x >> shift) & dmask], 1u);
+    }
+    for (int b = tid; b < kBins; b += NT) hist_next[b] = 0u;  // next pass's histogram
+    __syncthreads();
+    // Suffix counts: thread t owns bins [BPT*rt, BPT*rt + BPT) with rt = NT-1-t,
+    // so an exclusive scan in thread order counts the keys in higher bins.
+    const int rt = NT - 1 - tid;
+    uint32_t hb[BPT];
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      hb[e] = hist[BPT * rt + e];
+      c += (int)hb[e];
+    }
+    int tot;
+    const int above0 = block_exclusive_scan<NT>(c, lds_waves, tot);
+    if (above0 < remaining && above0 + c >= remaining) {
+      int above = above0;
+#pragma unroll
+      for (int e = BPT - 1; e >= 0; --e) {
+        if (above < remaining && above + (int)hb[e] >= remaining) {
+          bc[0] = BPT * rt + e;
+          bc[1] = remaining - above;
+          bc[2] = (int)hb[e];
+        }
+        above += (int)hb[e];
       }
-    } else {
-      for (int j = 0; j < cnt; ++j) {
-        const uint32_t x = kr[base + j];
-        if ((x & fixed) == prefix) atomicAdd(&hist[(x >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    prefix |= (uint32_t)bc[0] << shift;
+    fixed |= dmask << shift;
+    remaining = bc[1];
+    bucket_n = bc[2];
+    top = shift - 1;
+    ++npass;
+    __syncthreads();
+  }
+
+  // Single-wavefront finish: the boundary bucket (<= 256 keys) goes to LDS and
+  // one wavefront resolves the remaining bits one at a time with ballots.
+  if (top >= 0 && remaining != bucket_n) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const uint32_t x = kr.key(j);
+      const bool in_b = kr.valid(j) && (x & fixed) == prefix;
+      const unsigned long long m = __ballot(in_b);
+      if (m) {  // one LDS atomic per wavefront and round
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&bc[3], __popcll(m));
+        base = __shfl(base, 0);
+        if (in_b) bucket[base + (int)lane_prefix(m)] = x;
       }
     }
     __syncthreads();
     if (wave == 0) {
-      const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
-                     h3 = hist[4 * lane + 3];
-      const int c = (int)(h0 + h1 + h2 + h3);
-      int s = c;  // suffix sum: keys whose digit is >= 4 * lane
+      uint32_t v[kFinishMax / 64];
+      bool in[kFinishMax / 64];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int x = __shfl_down(s, off);
-        if (lane + off < 64) s += x;
+      for (int e = 0; e < kFinishMax / 64; ++e) {
+        const int idx = lane + 64 * e;
+        in[e] = idx < bucket_n;
+        v[e] = in[e] ? bucket[idx] : 0u;
       }
-      const unsigned long long ball = __ballot(s >= remaining);
-      const int lx = 63 - __clzll(ball);
-      if (lane == lx) {
-        int above = s - c;
-        const uint32_t hh[4] = {h0, h1, h2, h3};
-        int dsel = 4 * lane;
-        int need = remaining - above;
-        int cntd = (int)h0;
-        for (int e = 3; e >= 0; --e) {
-          if (above + (int)hh[e] >= remaining) {
-            dsel = 4 * lane + e;
-            need = remaining - above;
-            cntd = (int)hh[e];
-            break;
-          }
-          above += (int)hh[e];
+      int rem = remaining;
+      uint32_t pre = prefix, fx = fixed;
+      for (int bit = top; bit >= 0; --bit) {
+        const uint32_t bm = 1u << bit;
+        int ones = 0;
+#pragma unroll
+        for (int e = 0; e < kFinishMax / 64; ++e)
+          ones += __popcll(__ballot(in[e] && (v[e] & fx) == pre && (v[e] & bm)));
+        if (ones >= rem) {
+          pre |= bm;
+        } else {
+          rem -= ones;
         }
-        bc[0] = dsel;
-        bc[1] = need;
-        bc[2] = cntd;
+        fx |= bm;
+      }
+      int eq = 0;
+#pragma unroll
+      for (int e = 0; e < kFinishMax / 64; ++e) eq += __popcll(__ballot(in[e] && v[e] == pre));
+      if (lane == 0) {
+        bc[0] = (int)pre;
+        bc[1] = rem;
+        bc[2] = eq;
       }
     }
     __syncthreads();
-    const uint32_t dsel = (uint32_t)bc[0];
+    prefix = (uint32_t)bc[0];
+    fixed = 0xffffffffu;
     remaining = bc[1];
-    const int cntd = bc[2];
-    prefix |= dsel << shift;
-    fixed |= dmask << shift;
-    top = shift - 1;
-    if (remaining == cntd) break;  // the whole boundary bucket is taken
+    bucket_n = bc[2];
   }
 
-  // Keys whose fixed bits exceed `prefix` are taken; of those equal to it, the
-  // `remaining` lowest block ids.
-  int cgt = 0, ceq = 0;
-  for (int j = 0; j < cnt; ++j) {
-    const uint32_t x = key_at(j) & fixed;
-    cgt += x > prefix;
-    ceq += x == prefix;
-  }
-  int tot;
-  const int eq_before = block_exclusive_scan(ceq, lds_waves, tot);
-  int eq_quota = remaining - eq_before;
-  eq_quota = eq_quota < 0 ? 0 : (eq_quota > ceq ? ceq : eq_quota);
-  const int out_before = block_exclusive_scan(cgt + eq_quota, lds_waves, tot);
-  int pos = out_before;
-  int eq_seen = 0;
-  for (int j = 0; j < cnt; ++j) {
-    const uint32_t x = key_at(j) & fixed;
-    bool take = x > prefix;
-    if (x == prefix) {
-      take = eq_seen < eq_quota;
-      ++eq_seen;
+  // Output in ascending block order.  Keys whose fixed bits exceed `prefix`
+  // are taken; of the bucket_n keys equal to it, the `remaining` lowest ids.
+  // Round j of wavefront w covers blocks [NT j + 64 w, NT j + 64 w + 64), so a
+  // table of per-(round, wavefront) ballot counts, scanned once, gives every
+  // wavefront's output offset and a lane prefix count places each block.
+  const bool ties = remaining < bucket_n;
+  if constexpr (KPT > 0) {
+    int eq_rank_base[KPT];
+    if (ties) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const unsigned long long m = __ballot(kr.valid(j) && (kr.key(j) & fixed) == prefix);
+        if (lane == 0) tab[j * NW + wave] = __popcll(m);
+      }
+      __syncthreads();
+      if (wave == 0) wave_scan_table(tab, TAB);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) eq_rank_base[j] = tab[j * NW + wave];
+      __syncthreads();
     }
-    if (take) out[pos++] = base + j;
+    bool take[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) take[j] = kr.valid(j) && (kr.key(j) & fixed) >= prefix;
+    if (ties) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const bool is_eq = kr.valid(j) && (kr.key(j) & fixed) == prefix;
+        const unsigned long long m = __ballot(is_eq);
+        const int rank = eq_rank_base[j] + (int)lane_prefix(m);
+        if (is_eq) take[j] = rank < remaining;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const unsigned long long m = __ballot(take[j]);
+      if (lane == 0) tab[j * NW + wave] = __popcll(m);
+    }
+    __syncthreads();
+    if (wave == 0) wave_scan_table(tab, TAB);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const unsigned long long m = __ballot(take[j]);
+      const int pos = tab[j * NW + wave] + (int)lane_prefix(m);
+      if (take[j] && pos < k) out[pos] = tid + j * NT;
+    }
+  } else {
+    // Any number of rounds: one block scan per round.
+    int base_out = 0, base_eq = 0;
+    for (int j = 0; j < R; ++j) {
+      const bool v = kr.valid(j);
+      const uint32_t x = kr.key(j) & fixed;
+      const bool is_eq = v && x == prefix;
+      int tot_eq;
+      const int eq_before = block_exclusive_scan<NT>(is_eq ? 1 : 0, lds_waves, tot_eq);
+      const bool t = (v && x > prefix) || (is_eq && (!ties || base_eq + eq_before < remaining));
+      int tot;
+      const int pos = block_exclusive_scan<NT>(t ? 1 : 0, lds_waves, tot);
+      if (t && base_out + pos < k) out[base_out + pos] = tid + j * NT;
+      base_out += tot;
+      base_eq += tot_eq;
+    }
   }
 }
 
@@ -405,19 +604,17 @@ hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)a.H, (unsigned)a.R);
   const long long cand_max = a.max_blocks;
-  if (cand_max <= 8LL * kSelThreads) {
-    hipLaunchKernelGGL((select_kernel<8>), grid, dim3(kSelThreads), 0, stream, a.keys, a.seq_lens, a.sel_idx,
-                       a.sel_cnt, a.H, a.max_blocks, a.max_sel, a.budget_num, a.budget_den, a.min_blocks,
-                       a.local_blocks);
-  } else if (cand_max <= 32LL * kSelThreads) {
-    hipLaunchKernelGGL((select_kernel<32>), grid, dim3(kSelThreads), 0, stream, a.keys, a.seq_lens, a.sel_idx,
-                       a.sel_cnt, a.H, a.max_blocks, a.max_sel, a.budget_num, a.budget_den, a.min_blocks,
-                       a.local_blocks);
-  } else {
-    hipLaunchKernelGGL((select_kernel<0>), grid, dim3(kSelThreads), 0, stream, a.keys, a.seq_lens, a.sel_idx,
-                       a.sel_cnt, a.H, a.max_blocks, a.max_sel, a.budget_num, a.budget_den, a.min_blocks,
-                       a.local_blocks);
-  }
+#define RESA_SELECT_LAUNCH(NT, KPT)                                                                          \
+  hipLaunchKernelGGL((select_kernel<NT, KPT>), grid, dim3(NT), 0, stream, a.keys, a.seq_lens, a.sel_idx,      \
+                     a.sel_cnt, a.H, a.max_blocks, a.max_sel, a.budget_num, a.budget_den, a.min_blocks,      \
+                     a.local_blocks)
+  // 16 wavefronts: the select is latency-bound on one CU, and more resident
+  // wavefronts hide more of it than fewer, longer ones (measured).
+  if (cand_max <= 8LL * 1024) RESA_SELECT_LAUNCH(1024, 8);
+  else if (cand_max <= 16LL * 1024) RESA_SELECT_LAUNCH(1024, 16);
+  else if (cand_max <= 32LL * 1024) RESA_SELECT_LAUNCH(1024, 32);
+  else RESA_SELECT_LAUNCH(1024, 0);
+#undef RESA_SELECT_LAUNCH
   return hipGetLastError();
 }
 
