@@ -84,7 +84,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "resa_workspace_bytes": (sz, [cfgp, i32, i32, i32, i32, i32]),
         "resa_num_splits": (i32, [cfgp, i32, i32, i32, i32, i32]),
         "resa_build_descriptors": (i32, [cfgp, kvp, i32, vp, i32, vp]),
-        "resa_score_select": (i32, [cfgp, kvp, i32, vp, vp, vp, i32, vp, vp, sz, vp]),
+        "resa_score_select": (i32, [cfgp, kvp, i32, vp, i32, vp, vp, i32, vp, vp, sz, vp]),
         "resa_sparse_decode": (i32, [cfgp, kvp, i32, vp, vp, vp, i32, vp, vp, sz, vp]),
         "resa_dense_decode": (i32, [cfgp, kvp, i32, vp, vp, vp, sz, vp]),
         "resa_dense_rectify": (i32, [cfgp, kvp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
@@ -228,7 +228,8 @@ def build_descriptors(cfg: Config, kv: PagedKV, first_block: Optional[torch.Tens
 
 
 def score_select(cfg: Config, kv: PagedKV, q: torch.Tensor, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
-                 workspace: torch.Tensor, scores: Optional[torch.Tensor] = None) -> None:
+                 workspace: torch.Tensor, scores: Optional[torch.Tensor] = None,
+                 refresh_tail: bool = False) -> None:
     _check_cache(cfg, kv)
     R, H, G, d = kv.num_requests, cfg.num_kv_heads, cfg.group_size, cfg.head_dim
     _need(q, "q", cfg.torch_dtype, (R, H * G, d))
@@ -240,7 +241,8 @@ def score_select(cfg: Config, kv: PagedKV, q: torch.Tensor, sel_idx: torch.Tenso
     if scores is not None:
         _need(scores, "scores", torch.float32, (R, H, kv.max_blocks))
     c, k = cfg.c(), kv.c()
-    _call("resa_score_select", ctypes.byref(c), ctypes.byref(k), R, q.data_ptr(), sel_idx.data_ptr(),
+    _call("resa_score_select", ctypes.byref(c), ctypes.byref(k), R, q.data_ptr(), int(bool(refresh_tail)),
+          sel_idx.data_ptr(),
           sel_cnt.data_ptr(), int(sel_idx.shape[2]), _ptr(scores), workspace.data_ptr(), workspace.numel(),
           _stream_ptr())
 

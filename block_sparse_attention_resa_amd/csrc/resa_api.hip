@@ -216,10 +216,10 @@ resa_status resa_build_descriptors(const resa_config* cfg, const resa_paged_kv* 
 }
 
 resa_status resa_score_select(const resa_config* cfg, const resa_paged_kv* kv, int32_t num_requests, const void* q,
-                              int32_t* sel_idx, int32_t* sel_cnt, int32_t max_sel, float* scores, void* ws,
-                              size_t ws_bytes, void* stream) {
+                              int32_t refresh_tail, int32_t* sel_idx, int32_t* sel_cnt, int32_t max_sel,
+                              float* scores, void* ws, size_t ws_bytes, void* stream) {
   resa_status st = check_config(cfg);
-  if (st == RESA_OK) st = check_kv(kv, false, false, true);
+  if (st == RESA_OK) st = check_kv(kv, refresh_tail != 0, false, true);
   if (st == RESA_OK) st = check_requests(num_requests);
   if (st != RESA_OK) return st;
   if (!q || !aligned16(q) || !sel_idx || !sel_cnt) return RESA_ERR_INVALID_ARG;
@@ -233,6 +233,8 @@ resa_status resa_score_select(const resa_config* cfg, const resa_paged_kv* kv, i
   ScoreArgs sa{};
   sa.q = q;
   sa.desc_pool = kv->desc_pool;
+  sa.k_pool = kv->k_pool;
+  sa.refresh_tail = refresh_tail != 0;
   sa.table = kv->block_table;
   sa.seq_lens = kv->seq_lens;
   sa.keys = static_cast<uint32_t*>(ws);

@@ -71,6 +71,8 @@ hipError_t launch_descriptors(const DescArgs& a, hipStream_t stream);
 struct ScoreArgs {
   const void* q;
   const void* desc_pool;
+  const void* k_pool;  // read when refresh_tail
+  int32_t refresh_tail;
   const int32_t* table;
   const int32_t* seq_lens;
   uint32_t* keys;  // [R][H][max_blocks] workspace

@@ -26,6 +26,7 @@
 // the threshold are taken, blocks equal to it lowest index first, and one
 // scanned table of per-(round, wavefront) ballot counts places every selected
 // id in ascending order.
+#include "desc_unit.h"
 #include "resa_internal.h"
 
 namespace resa {
@@ -77,11 +78,12 @@ struct ChunkLoad<float> {
 constexpr int kScoreUnroll = 4;
 
 template <typename T, int D, int MODE, int MAXG>
-__global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, const T* __restrict__ desc,
+__global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, const T* desc,
                                                     const int32_t* __restrict__ table,
                                                     const int32_t* __restrict__ seq_lens,
                                                     uint32_t* __restrict__ keys, float* __restrict__ scores, int H,
-                                                    int G, int max_blocks, int num_pool_blocks) {
+                                                    int G, int max_blocks, int num_pool_blocks,
+                                                    const T* __restrict__ k_pool, T* desc_tail, int score_wgs) {
   using CL = ChunkLoad<T>;
   constexpr int VPL = CL::kVals;
   constexpr int CH = 2 * D / VPL;  // lanes per descriptor
@@ -90,6 +92,20 @@ __global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, co
 
   const int r = blockIdx.y;
   const int t = threadIdx.x;
+  if ((int)blockIdx.x >= score_wgs) {
+    // Tail refresh: the extra workgroup recomputes the descriptor of each KV
+    // head's last block (the block the newest token was appended to).  The
+    // last block is always selected, so the score the other workgroups read
+    // for it concurrently is never used.
+    const int L = clampi(seq_lens[r], 0, max_blocks * kBlock);
+    const int M = (L + kBlock - 1) / kBlock;
+    if (M == 0) return;
+    const int p = clampi(table[(size_t)r * max_blocks + M - 1], 0, num_pool_blocks - 1);
+    for (int i = t >> 6; i < H; i += (int)(blockDim.x >> 6))
+      descriptor_unit<T, D>(k_pool + ((size_t)p * H + i) * kBlock * D, desc_tail + ((size_t)p * H + i) * 2 * D,
+                            L - (M - 1) * kBlock);
+    return;
+  }
   const int lane = t & 63;
   const int grp = t / CH;
   const int lg = t % CH;
@@ -227,11 +243,12 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
   const int blocks_per_wg = bpi * kScoreUnroll;  // <= 64: one table entry per lane
   const int wgs = (a.max_blocks + blocks_per_wg - 1) / blocks_per_wg;
   const size_t lds = (size_t)a.H * 2 * D * sizeof(float);
-  dim3 grid((unsigned)wgs, (unsigned)a.R);
+  dim3 grid((unsigned)(wgs + (a.refresh_tail ? 1 : 0)), (unsigned)a.R);
 #define RESA_SCORE_LAUNCH(MODE, MAXG)                                                                        \
   hipLaunchKernelGGL((score_kernel<T, D, MODE, MAXG>), grid, dim3(threads), lds, stream,                     \
                      static_cast<const T*>(a.q), static_cast<const T*>(a.desc_pool), a.table, a.seq_lens, a.keys, \
-                     a.scores, a.H, a.G, a.max_blocks, a.num_pool_blocks)
+                     a.scores, a.H, a.G, a.max_blocks, a.num_pool_blocks, static_cast<const T*>(a.k_pool),  \
+                     static_cast<T*>(const_cast<void*>(a.desc_pool)), wgs)
   if (a.G <= 8) {
     if (a.mode == 0) RESA_SCORE_LAUNCH(0, 8);
     else RESA_SCORE_LAUNCH(1, 8);

@@ -31,8 +31,9 @@
  *   no access leaves the buffers described below: a sequence length outside
  *   [0, max_blocks*16] is clamped into it, a block-table entry outside
  *   [0, num_pool_blocks) is clamped into it, a selected block id outside
- *   [0, M) is clamped into it.  Such inputs give unspecified results, never
- *   an out-of-bounds access.  Requests with sequence length 0 produce a zero
+ *   [0, max_blocks) is clamped into it (rows at or past the sequence length
+ *   never contribute).  Such inputs give unspecified results, never an
+ *   out-of-bounds access.  Requests with sequence length 0 produce a zero
  *   output and an empty selection.
  * - Rows of the last block at positions >= the sequence length may hold any
  *   bit pattern (NaN included); no result depends on them.
@@ -168,6 +169,12 @@ resa_status resa_build_descriptors(const resa_config* cfg, const resa_paged_kv* 
  * every block from desc_pool and q (score_mode), then selects
  * n = resa_selection_count(cfg, M) blocks: the local_blocks most recent blocks
  * always, and the highest-scoring older blocks (ties: lower block id first).
+ * refresh_tail != 0 also recomputes, from k_pool, the descriptor of block
+ * M-1 of every request and KV head (the block the newest token was appended
+ * to: Algorithm 1's incremental block-key-cache update) in the same launch;
+ * it then equals what resa_build_descriptors(cfg, kv, R, NULL, 1, ...) writes.
+ * That block is always selected, so its score does not influence the
+ * selection; its exported score is unspecified when refresh_tail != 0.
  *   sel_idx [R][H][max_sel] int32   selected logical block ids, ascending,
  *                                   entries [n, max_sel) set to -1
  *   sel_cnt [R][H] int32            n
@@ -175,12 +182,13 @@ resa_status resa_build_descriptors(const resa_config* cfg, const resa_paged_kv* 
  *                                   score; entries >= M are left untouched
  * Requires max_sel >= resa_selection_count(cfg, kv->max_blocks) and
  * ws_bytes >= resa_workspace_bytes(cfg, RESA_OP_SCORE_SELECT, ...).
- * Reads q, desc_pool, block_table, seq_lens.
+ * Reads q, desc_pool, block_table, seq_lens (and k_pool, writing the last
+ * block's descriptor in desc_pool, when refresh_tail != 0).
  */
 resa_status resa_score_select(const resa_config* cfg, const resa_paged_kv* kv,
-                              int32_t num_requests, const void* q, int32_t* sel_idx,
-                              int32_t* sel_cnt, int32_t max_sel, float* scores, void* ws,
-                              size_t ws_bytes, void* stream);
+                              int32_t num_requests, const void* q, int32_t refresh_tail,
+                              int32_t* sel_idx, int32_t* sel_cnt, int32_t max_sel,
+                              float* scores, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Group block sparse attention (Eq 2, masked positions excluded from the

@@ -148,8 +148,8 @@ def test_score_select_argument_checks(lib):
     kv = kv_ok()
     n_full = lib.resa_selection_count(ctypes.byref(c), 32)
     ws = lib.resa_workspace_bytes(ctypes.byref(c), B.OP_SCORE_SELECT, 1, 32, n_full, 0)
-    call = lambda q, si, sc, ms, wsp, wsb: lib.resa_score_select(  # noqa: E731
-        ctypes.byref(c), ctypes.byref(kv), 1, q, si, sc, ms, None, wsp, wsb, None)
+    call = lambda q, si, sc, ms, wsp, wsb, rt=0: lib.resa_score_select(  # noqa: E731
+        ctypes.byref(c), ctypes.byref(kv), 1, q, rt, si, sc, ms, None, wsp, wsb, None)
     assert call(None, FAKE, FAKE, n_full, FAKE, ws) == 1
     assert call(FAKE_ODD, FAKE, FAKE, n_full, FAKE, ws) == 1
     assert call(FAKE, None, FAKE, n_full, FAKE, ws) == 1
@@ -157,6 +157,8 @@ def test_score_select_argument_checks(lib):
     assert call(FAKE, FAKE, FAKE, n_full - 1, FAKE, ws) == 1  # sel_idx rows too short
     assert call(FAKE, FAKE, FAKE, n_full, None, ws) == 3
     assert call(FAKE, FAKE, FAKE, n_full, FAKE, ws - 1) == 3
+    kv.k_pool = None  # the tail refresh reads k_pool
+    assert call(FAKE, FAKE, FAKE, n_full, FAKE, ws, 1) == 1
 
 
 def test_decode_argument_checks(lib):

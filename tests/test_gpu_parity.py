@@ -94,6 +94,29 @@ def test_descriptor_ranges_tail_and_first_block(name):
                 assert bool((case.kv.desc_pool[p] == 3.0).all())
 
 
+@pytest.mark.parametrize("name", ["bf16_d128_L647", "bf16_ragged_r3_perm_nan", "tiny_f32_ctx2k",
+                                  "bf16_budget3_local3"])
+def test_score_select_refreshes_tail_descriptor(name):
+    case = make(name)
+    C.run_descriptors(case)
+    full = case.kv.desc_pool.clone()
+    sel_ref, cnt_ref, _ = C.run_score_select(case, with_scores=False)
+    # spoil the last block's descriptor of every request; the fused refresh restores it
+    for r, L in enumerate(case.inp.seq_lens):
+        p = int(case.kv.block_table[r, num_blocks(L) - 1])
+        case.kv.desc_pool[p] = 7.0
+    R, H = case.R, case.spec.num_kv_heads
+    ms = C.max_sel_for(case)
+    sel_idx = torch.full((R, H, ms), -7, dtype=torch.int32, device="cuda")
+    sel_cnt = torch.full((R, H), -7, dtype=torch.int32, device="cuda")
+    ws = resa.alloc_workspace(case.cfg, resa.OP_SCORE_SELECT, R, case.kv.max_blocks, ms)
+    resa.score_select(case.cfg, case.kv, case.inp.q, sel_idx, sel_cnt, ws, refresh_tail=True)
+    torch.cuda.synchronize()
+    assert torch.equal(C.desc_bits(case.kv.desc_pool), C.desc_bits(full))
+    # the tail block is forced, so its (spoiled) score cannot change the selection
+    assert torch.equal(sel_idx, sel_ref) and torch.equal(sel_cnt, cnt_ref)
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_score_select_parity(name):
     case = make(name)
