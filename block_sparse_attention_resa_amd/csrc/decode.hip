@@ -8,10 +8,10 @@
 // of each KV block per GQA group shared by all of its query heads).
 //
 // Work decomposition.  Grid (splits, KV heads, requests).  The block list of
-// one (request, KV head) is cut into `splits` equal ranges, one per
-// 256-thread workgroup; the workgroup's four wavefronts take consecutive
-// sub-ranges and each keeps its own online-softmax state, merged through LDS
-// at the end into one partial (m, l, o) per query head.  A second kernel
+// one (request, KV head) is cut into `splits` equal ranges, one per workgroup
+// of 8 wavefronts (about one workgroup per CU); the wavefronts take
+// consecutive sub-ranges and each keeps its own online-softmax state, merged
+// through LDS into one partial (m, l, o) per query head.  A second kernel
 // merges the splits' partials with their log-sum-exp weights.
 //
 // Matrix cores.  Per 16-token block a wavefront computes the transposed score
@@ -42,8 +42,6 @@
 namespace resa {
 namespace {
 
-constexpr int kDecodeWaves = 4;
-constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kChunk = 2;  // blocks per pipelined chunk
 
 template <typename T, int D>
@@ -52,17 +50,27 @@ struct Chunk {
   int blk[kChunk];  // logical block id, -1 = empty slot
 };
 
-template <typename T, int D, bool SPARSE>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
+// Query columns merged per LDS pass inside a workgroup (LDS stays ~34 KiB).
+template <int NW>
+struct DecodeShape {
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kCols = NW <= 8 ? 8 : 4;
+};
+
+template <typename T, int D, bool SPARSE, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k_pool, const T* __restrict__ v_pool,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, int max_sel, float* __restrict__ part_o, float* __restrict__ part_ml,
     int H, int G, int max_blocks, int num_pool_blocks, int S, float scale_log2) {
   using F = Frag<T, D>;
+  using SH = DecodeShape<NW>;
   constexpr int NT = F::NT;
-  __shared__ float s_acc[kDecodeWaves][16][D + 4];
-  __shared__ float s_m[kDecodeWaves][16];
-  __shared__ float s_l[kDecodeWaves][16];
+  constexpr int NTH = SH::kThreads;
+  constexpr int CG = SH::kCols;
+  __shared__ float s_acc[NW][CG][D + 4];
+  __shared__ float s_m[NW][16];
+  __shared__ float s_l[NW][16];
 
   const int s = blockIdx.x;
   const int i = blockIdx.y;
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   // The split and wavefront ranges depend only on the list capacity, so the
   // block-id loads below do not wait for sel_cnt; n only trims the range.
   const int beg = s * bps;
-  const int per = (bps + kDecodeWaves - 1) / kDecodeWaves;
+  const int per = (bps + NW - 1) / NW;
   const int cap = SPARSE ? max_sel : max_blocks;
   const int wb = beg + wave * per;
   const int we_cap = min(min(beg + bps, cap), wb + per);  // positions readable without n
@@ -190,47 +198,58 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     }
   }
 
+  // ---- merge the wavefronts of this workgroup into one partial (m, l, o) per column
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-    *reinterpret_cast<floatx4_t*>(&s_acc[wave][col][16 * t + 4 * quad]) = acc[t];
   if (quad == 0) {
     s_m[wave][col] = m_run;
     s_l[wave][col] = l_run;
   }
-  __syncthreads();
-
   const size_t prow = ((size_t)r * H + i) * S + s;  // partial row of this workgroup
-  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
-    const int j = idx / D;
-    const int c = idx % D;
-    float mw = -INFINITY;
+  for (int c0 = 0; c0 < G; c0 += CG) {
+    if (col >= c0 && col < c0 + CG) {
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) mw = fmaxf(mw, s_m[w][j]);
-    float o = 0.f, l = 0.f;
-    if (mw != -INFINITY) {
+      for (int t = 0; t < NT; ++t)
+        *reinterpret_cast<floatx4_t*>(&s_acc[wave][col - c0][16 * t + 4 * quad]) = acc[t];
+    }
+    __syncthreads();
+    const int ncols = min(CG, G - c0);
+    for (int idx = threadIdx.x; idx < ncols * D; idx += NTH) {
+      const int jl = idx / D;
+      const int j = c0 + jl;
+      const int c = idx % D;
+      float mw = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        const float wt = exp2f(s_m[w][j] - mw);
-        o += wt * s_acc[w][j][c];
-        l += wt * s_l[w][j];
+      for (int w = 0; w < NW; ++w) mw = fmaxf(mw, s_m[w][j]);
+      float o = 0.f, l = 0.f;
+      if (mw != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float wt = exp2f(s_m[w][j] - mw);
+          o += wt * s_acc[w][jl][c];
+          l += wt * s_l[w][j];
+        }
+      }
+      part_o[(prow * G + j) * D + c] = o;
+      if (c == 0) {
+        part_ml[(prow * G + j) * 2] = mw;
+        part_ml[(prow * G + j) * 2 + 1] = l;
       }
     }
-    part_o[(prow * G + j) * D + c] = o;
-    if (c == 0) {
-      part_ml[(prow * G + j) * 2] = mw;
-      part_ml[(prow * G + j) * 2 + 1] = l;
-    }
+    __syncthreads();
   }
+
 }
 
 // Log-sum-exp merge of split partials.  One workgroup per output row:
 //   out[c] = sum_s 2^(m_s - m) o_s[c] / sum_s 2^(m_s - m) l_s,  m = max_s m_s.
-// The split weights are computed once into LDS; the weighted sum is spread
-// over (channel quad, split subset) pairs so every thread issues a batch of
-// independent 16-byte loads, then reduced through LDS.
+// Every load of a batch (the row's m_s, l_s and the partial outputs) is issued
+// before the first reduction, so a batch of up to kMergeBatch splits costs one
+// memory round trip.  Thread (g, c4) sums splits g, g + NG, ... of channel
+// quad c4 in increasing order; the NG group sums are added in group order, so
+// the result is deterministic.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 16;  // splits per thread held in registers per batch
 
 __device__ __forceinline__ float block_reduce(float v, float* lds, bool is_max) {
   const int lane = threadIdx.x & 63;
@@ -254,8 +273,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
                                                               const float* __restrict__ part_ml,
                                                               float* __restrict__ out, int H, int G, int S,
                                                               int rows_per_head, int row_stride_out) {
-  constexpr int C4 = D / 4;                  // float4 lanes per row
-  constexpr int NG = kMergeThreads / C4;     // split subsets
+  constexpr int C4 = D / 4;               // float4 lanes per row
+  constexpr int NG = kMergeThreads / C4;  // split groups
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[kMergeThreads / 64];
   __shared__ floatx4_t s_acc[kMergeThreads];
@@ -263,45 +282,48 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   const int i = blockIdx.y;
   const int r = blockIdx.z;
   const int tid = threadIdx.x;
+  const int c4 = tid % C4;
+  const int grp = tid / C4;
   const size_t base = ((size_t)r * H + i) * S;
 
-  float m = -INFINITY;
-  float lv[kMaxSplits / kMergeThreads];
+  float mv[kMaxSplits / kMergeThreads], lv[kMaxSplits / kMergeThreads];
 #pragma unroll
   for (int k = 0; k < kMaxSplits / kMergeThreads; ++k) {
     const int s = tid + k * kMergeThreads;
-    lv[k] = 0.f;
-    if (s < S) {
-      const size_t pr = (base + s) * rows_per_head + row;
-      const float ms = part_ml[pr * 2];
-      lv[k] = part_ml[pr * 2 + 1];
-      s_w[s] = ms;
-      m = fmaxf(m, ms);
-    }
+    const size_t pr = (base + (s < S ? s : 0)) * rows_per_head + row;
+    mv[k] = s < S ? part_ml[pr * 2] : -INFINITY;
+    lv[k] = s < S ? part_ml[pr * 2 + 1] : 0.f;
   }
+  floatx4_t ov[kMergeBatch];
+#pragma unroll
+  for (int b = 0; b < kMergeBatch; ++b) {
+    const int s = grp + b * NG;
+    ov[b] = s < S ? *reinterpret_cast<const floatx4_t*>(part_o + ((base + s) * rows_per_head + row) * D + 4 * c4)
+                  : floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMaxSplits / kMergeThreads; ++k) m = fmaxf(m, mv[k]);
   m = block_reduce(m, s_red, true);
   float den = 0.f;
 #pragma unroll
   for (int k = 0; k < kMaxSplits / kMergeThreads; ++k) {
     const int s = tid + k * kMergeThreads;
-    if (s < S) {
-      const float ms = s_w[s];
-      const float w = (m == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - m);
-      s_w[s] = w;
-      den += w * lv[k];
-    }
+    const float w = (m == -INFINITY || mv[k] == -INFINITY) ? 0.f : exp2f(mv[k] - m);
+    if (s < S) s_w[s] = w;
+    den += w * lv[k];
   }
   den = block_reduce(den, s_red, false);  // its barriers also publish s_w
 
-  const int c4 = tid % C4;
-  const int grp = tid / C4;
   floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = grp; s < S; s += NG) {
-    const float w = s_w[s];
-    const floatx4_t o = *reinterpret_cast<const floatx4_t*>(part_o + ((base + s) * rows_per_head + row) * D + 4 * c4);
-    acc += w * o;
+#pragma unroll
+  for (int b = 0; b < kMergeBatch; ++b) {
+    const int s = grp + b * NG;
+    if (s < S) acc += s_w[s] * ov[b];
   }
+  for (int s = grp + kMergeBatch * NG; s < S; s += NG)  // splits beyond one batch (large S)
+    acc += s_w[s] * *reinterpret_cast<const floatx4_t*>(part_o + ((base + s) * rows_per_head + row) * D + 4 * c4);
   s_acc[tid] = acc;
   __syncthreads();
   if (grp == 0) {
@@ -316,19 +338,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int NW>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)a.splits, (unsigned)a.H, (unsigned)a.R);
+  dim3 block(64 * NW);
   if (a.sel_idx) {
-    hipLaunchKernelGGL((decode_kernel<T, D, true>), grid, dim3(kDecodeThreads), 0, stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
-                       static_cast<const T*>(a.v_pool), a.table, a.seq_lens, a.sel_idx, a.sel_cnt, a.max_sel,
-                       a.part_o, a.part_ml, a.H, a.G, a.max_blocks, a.num_pool_blocks, a.splits, a.scale_log2);
+    hipLaunchKernelGGL((decode_kernel<T, D, true, NW>), grid, block, 0, stream, static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.k_pool), static_cast<const T*>(a.v_pool), a.table, a.seq_lens,
+                       a.sel_idx, a.sel_cnt, a.max_sel, a.part_o, a.part_ml, a.H, a.G, a.max_blocks,
+                       a.num_pool_blocks, a.splits, a.scale_log2);
   } else {
-    hipLaunchKernelGGL((decode_kernel<T, D, false>), grid, dim3(kDecodeThreads), 0, stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
-                       static_cast<const T*>(a.v_pool), a.table, a.seq_lens, nullptr, nullptr, 0, a.part_o,
-                       a.part_ml, a.H, a.G, a.max_blocks, a.num_pool_blocks, a.splits, a.scale_log2);
+    hipLaunchKernelGGL((decode_kernel<T, D, false, NW>), grid, block, 0, stream, static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.k_pool), static_cast<const T*>(a.v_pool), a.table, a.seq_lens,
+                       nullptr, nullptr, 0, a.part_o, a.part_ml, a.H, a.G, a.max_blocks, a.num_pool_blocks,
+                       a.splits, a.scale_log2);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -350,9 +373,11 @@ hipError_t launch_merge(const float* part_o, const float* part_ml, float* out, i
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  // fp32 fragments need twice the registers: 4 wavefronts per workgroup keeps them spill-free
   if (a.dtype == 0)
-    return a.D == 128 ? launch_decode_t<bf16_t, 128>(a, stream) : launch_decode_t<bf16_t, 64>(a, stream);
-  return a.D == 128 ? launch_decode_t<float, 128>(a, stream) : launch_decode_t<float, 64>(a, stream);
+    return a.D == 128 ? launch_decode_t<bf16_t, 128, kDecodeWaves>(a, stream)
+                      : launch_decode_t<bf16_t, 64, kDecodeWaves>(a, stream);
+  return a.D == 128 ? launch_decode_t<float, 128, 4>(a, stream) : launch_decode_t<float, 64, 4>(a, stream);
 }
 
 }  // namespace resa

@@ -73,12 +73,12 @@ int splits_for(const resa_config* c, int op, int R, int max_blocks, int max_sel,
   long long len, target, min_share;
   if (op == RESA_OP_SPARSE_DECODE) {
     len = max_sel;
-    target = 512;
-    min_share = 4;
+    target = 256;  // 8-wavefront workgroups: about one per CU
+    min_share = kDecodeWaves;
   } else if (op == RESA_OP_DENSE_DECODE) {
     len = max_blocks;
-    target = 512;
-    min_share = 16;
+    target = 256;
+    min_share = 8 * kDecodeWaves;
   } else {  // rectify
     const long long rg = ceil_div((long long)chunk * c->group_size, 64);
     len = max_blocks;
@@ -95,8 +95,8 @@ int splits_for(const resa_config* c, int op, int R, int max_blocks, int max_sel,
     if (s > cap) s = cap;
   }
   if (s > len) s = len;
-  if (s < 1) s = 1;
   if (s > kMaxSplits) s = kMaxSplits;
+  if (s < 1) s = 1;
   return (int)s;
 }
 

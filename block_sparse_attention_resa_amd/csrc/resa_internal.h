@@ -11,6 +11,7 @@ namespace resa {
 
 constexpr int kBlock = 16;       // tokens per KV block
 constexpr int kMaxSplits = 1024;  // split partials one merge workgroup combines
+constexpr int kDecodeWaves = 8;   // wavefronts per decode workgroup
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) short short4_t;
@@ -101,8 +102,8 @@ struct DecodeArgs {
   const int32_t* sel_cnt;  // null for dense
   int32_t max_sel;
   float* out;
-  float* part_o;   // [R][H][S][G][D]
-  float* part_ml;  // [R][H][S][G][2]
+  float* part_o;       // [R][H][S][G][D]
+  float* part_ml;      // [R][H][S][G][2]
   int32_t R, H, G, D, dtype, max_blocks, num_pool_blocks, splits;
   float scale_log2;  // sm_scale * log2(e)
 };

@@ -135,7 +135,9 @@ int32_t resa_selection_count(const resa_config* cfg, int32_t num_blocks);
 
 /* Bytes of workspace `op` needs for `num_requests` requests of up to
  * `max_blocks` blocks; `max_sel` is the sel_idx row capacity (sparse ops) and
- * `chunk` the rectification window (rectify).  Returns 0 on invalid arguments. */
+ * `chunk` the rectification window (rectify).  Returns 0 on invalid arguments.
+ * Workspace contents need no initialisation; calls that share a workspace
+ * must be ordered on one stream. */
 size_t resa_workspace_bytes(const resa_config* cfg, int32_t op, int32_t num_requests,
                             int32_t max_blocks, int32_t max_sel, int32_t chunk);
 
