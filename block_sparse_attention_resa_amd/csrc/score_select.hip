@@ -20,12 +20,14 @@
 // Selection.  One 1024-thread workgroup per (request, KV head); thread t
 // owns candidate blocks t, t + 1024, ... (coalesced loads, kept in
 // registers).  The (n - n_local)-th largest key among the older blocks is
-// found MSB-first over the bits in which the candidates differ: 11-bit
-// histogram passes in LDS narrow the boundary bucket to at most 256 keys, then
-// one wavefront resolves the remaining bits with ballot counts.  Blocks above
-// the threshold are taken, blocks equal to it lowest index first, and one
-// scanned table of per-(round, wavefront) ballot counts places every selected
-// id in ascending order.
+// found by histogram passes in LDS over monotone bin maps: the first pass
+// bins the score range [min, max] into 2048 equal-width bins, later passes
+// (rarely needed) bin the key offsets inside the boundary bucket.  Once the
+// boundary bucket holds at most 256 keys they are packed into LDS and ranked
+// in parallel.  Blocks above the threshold are taken, blocks equal to it
+// lowest index first, and one scanned table of per-(round, wavefront) ballot
+// counts places every selected id in ascending order.  Wave-wide scans and
+// reductions use DPP lane shifts.
 #include "desc_unit.h"
 #include "resa_internal.h"
 
@@ -264,10 +266,48 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
 
 constexpr int kDigitBits = 11;  // histogram pass: 2048 bins
 constexpr int kBins = 1 << kDigitBits;
-constexpr int kFinishMax = 256;  // boundary bucket size the single-wavefront finish takes
+constexpr int kFinishMax = 256;  // boundary bucket size the ranking finish takes
 
 __device__ __forceinline__ unsigned lane_prefix(unsigned long long mask) {
   return __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
+}
+
+// Cross-lane steps through DPP (row shifts within 16-lane rows, then the
+// row-15 / row-31 broadcasts), which stay in the vector ALU instead of the
+// LDS crossbar.  Lanes that have no source receive `id`.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t id, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  uint32_t v = (uint32_t)x;
+  v += dpp_u32<0x111>(0u, v);  // row_shr:1
+  v += dpp_u32<0x112>(0u, v);  // row_shr:2
+  v += dpp_u32<0x114>(0u, v);  // row_shr:4
+  v += dpp_u32<0x118>(0u, v);  // row_shr:8
+  v += dpp_u32<0x142, 0xa>(0u, v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_u32<0x143, 0xc>(0u, v);  // row_bcast:31 into rows 2 and 3
+  return (int)v;
+}
+
+// Minimum and maximum over the 64 lanes, returned in every lane.
+__device__ __forceinline__ void wave_min_max(uint32_t& mn, uint32_t& mx) {
+  mn = min(mn, dpp_u32<0x111>(0xffffffffu, mn));
+  mx = max(mx, dpp_u32<0x111>(0u, mx));
+  mn = min(mn, dpp_u32<0x112>(0xffffffffu, mn));
+  mx = max(mx, dpp_u32<0x112>(0u, mx));
+  mn = min(mn, dpp_u32<0x114>(0xffffffffu, mn));
+  mx = max(mx, dpp_u32<0x114>(0u, mx));
+  mn = min(mn, dpp_u32<0x118>(0xffffffffu, mn));
+  mx = max(mx, dpp_u32<0x118>(0u, mx));
+  mn = min(mn, dpp_u32<0x142, 0xa>(0xffffffffu, mn));
+  mx = max(mx, dpp_u32<0x142, 0xa>(0u, mx));
+  mn = min(mn, dpp_u32<0x143, 0xc>(0xffffffffu, mn));
+  mx = max(mx, dpp_u32<0x143, 0xc>(0u, mx));
+  mn = (uint32_t)__builtin_amdgcn_readlane((int)mn, 63);
+  mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
 }
 
 // Exclusive prefix sum over the workgroup in thread order; `total` gets the sum.
@@ -276,12 +316,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& 
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int n = __shfl_up(incl, off);
-    if (lane >= off) incl += n;
-  }
+  const int incl = wave_incl_sum(v);
   if (lane == 63) lds_waves[wave] = incl;
   __syncthreads();
   int before = 0;
@@ -294,6 +329,27 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& 
   }
   __syncthreads();
   return before + incl - v;
+}
+
+template <int NT>
+__device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, uint32_t* lds_min, uint32_t* lds_max) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  wave_min_max(mn, mx);
+  if (lane == 0) {
+    lds_min[wave] = mn;
+    lds_max[wave] = mx;
+  }
+  __syncthreads();
+  mn = 0xffffffffu;
+  mx = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mn = min(mn, lds_min[w]);
+    mx = max(mx, lds_max[w]);
+  }
+  __syncthreads();  // lds_min / lds_max may be rewritten right after
 }
 
 // In-place exclusive prefix sum of tab[0, n), n <= 512, by one wavefront:
@@ -309,13 +365,7 @@ __device__ __forceinline__ void wave_scan_table(int* tab, int n) {
     v[e] = (e < per && idx < n) ? tab[idx] : 0;
     sum += v[e];
   }
-  int incl = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int x = __shfl_up(incl, off);
-    if (lane >= off) incl += x;
-  }
-  int run = incl - sum;
+  int run = wave_incl_sum(sum) - sum;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int idx = lane * per + e;
@@ -326,23 +376,29 @@ __device__ __forceinline__ void wave_scan_table(int* tab, int n) {
 
 // Candidate keys of one (request, KV head).  Thread t owns blocks t + NT*j,
 // so every load instruction of a wavefront reads 256 contiguous bytes.  KPT > 0
-// keeps up to KPT rounds in registers; KPT == 0 re-reads the row (any size).
+// keeps KPT rounds in registers, loaded before the request's length is known
+// (indices clamped into the row); KPT == 0 re-reads the row (any size).
 template <int NT, int KPT>
 struct KeyRuns {
   uint32_t reg[KPT > 0 ? KPT : 1];
   const uint32_t* row;
   int C, rounds;
-  __device__ void load(const uint32_t* kr, int c) {
+  unsigned long long in_mask;  // KPT > 0: bit j set when this lane's key of round j is a candidate
+  __device__ void prefetch(const uint32_t* kr, int row_len) {
     row = kr;
-    C = c;
-    rounds = (c + NT - 1) / NT;
     if constexpr (KPT > 0) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const int idx = threadIdx.x + j * NT;
-        reg[j] = kr[idx < c ? idx : c - 1];
+        reg[j] = kr[idx < row_len ? idx : row_len - 1];
       }
     }
+  }
+  __device__ void set_count(int c) {
+    C = c;
+    rounds = (c + NT - 1) / NT;
+    const int mine = c > (int)threadIdx.x ? (c - (int)threadIdx.x + NT - 1) / NT : 0;  // rounds with a candidate
+    in_mask = mine >= 64 ? ~0ull : (1ull << mine) - 1ull;
   }
   __device__ bool valid(int j) const { return j < rounds && (int)threadIdx.x + j * NT < C; }
   __device__ uint32_t key(int j) const {
@@ -350,6 +406,79 @@ struct KeyRuns {
     else return row[threadIdx.x + j * NT];
   }
   __device__ int nrounds() const { return KPT > 0 ? KPT : rounds; }
+};
+
+// Runs the statements in the variadic argument for every round j of `kr`,
+// with `in` telling whether the lane's key of that round is a candidate.
+// Expects NT, KPT and a KeyRuns `kr` in scope.
+#define RESA_FOR_KEYS(...)                                                       \
+  do {                                                                           \
+    if constexpr (KPT > 0) {                                                     \
+      _Pragma("unroll") for (int j = 0; j < KPT; ++j) {                          \
+        const bool in = (kr.in_mask >> j) & 1ull;                                \
+        __VA_ARGS__                                                              \
+      }                                                                          \
+    } else {                                                                     \
+      for (int j = 0; j < kr.rounds; ++j) {                                      \
+        const bool in = (int)threadIdx.x + j * NT < kr.C;                        \
+        __VA_ARGS__                                                              \
+      }                                                                          \
+    }                                                                            \
+  } while (0)
+
+// Monotone map of a key onto kBins histogram bins, built for a bucket whose
+// keys lie in [lo, hi] (keys outside are clamped to the end bins).  By value:
+// bins of equal width in score, which spreads any finite score distribution
+// evenly.  By key: the key offset shifted right, which always separates lo
+// from hi and shrinks the range 2^11-fold per pass; over a range inside one
+// sign and at most two binades it is within 2x of equal width in score and
+// costs fewer instructions, so the first pass uses it there.
+struct BinMap {
+  bool by_value;
+  float fmin, scale;
+  uint32_t lo, hi;
+  int shift;
+  __device__ void init(uint32_t lo_key, uint32_t hi_key, bool allow_value) {
+    lo = lo_key;
+    hi = hi_key;
+    const uint32_t d = hi_key - lo_key;
+    const int nb = d ? 32 - __clz(d) : 0;
+    shift = nb > kDigitBits ? nb - kDigitBits : 0;
+    by_value = false;
+    fmin = 0.f;
+    scale = 0.f;
+    // same sign and exponents at most one apart: key order is near-linear in score
+    const bool narrow = ((lo_key ^ hi_key) >> 31) == 0u && ((hi_key >> 23) - (lo_key >> 23)) <= 1u;
+    if (allow_value && !narrow) {
+      const float a = __uint_as_float(u32_from_order_key(lo_key));
+      const float b = __uint_as_float(u32_from_order_key(hi_key));
+      const float range = b - a;
+      const float s = (float)kBins / range;
+      // lo lands in bin 0; hi must land in bin >= 1 so every pass makes progress
+      if (__builtin_isfinite(a) && __builtin_isfinite(b) && __builtin_isfinite(range) && range > 0.f &&
+          __builtin_isfinite(s) && range * s >= 1.f) {
+        by_value = true;
+        fmin = a;
+        scale = s;
+      }
+    }
+  }
+  __device__ int value_bin(uint32_t key) const {
+    const float f = __uint_as_float(u32_from_order_key(min(max(key, lo), hi)));
+    const int b = (int)((f - fmin) * scale);
+    return min(max(b, 0), kBins - 1);
+  }
+  __device__ int key_bin(uint32_t key) const { return (int)((min(max(key, lo), hi) - lo) >> shift); }
+  __device__ int operator()(uint32_t key) const { return by_value ? value_bin(key) : key_bin(key); }
+};
+
+// Candidates still in play: keys in [lo, hi] and, after a pass whose range was
+// not re-measured, in histogram bin `bin` of `map`.
+struct Bucket {
+  uint32_t lo, hi;
+  BinMap map;
+  int bin;  // -1: no bin condition
+  __device__ bool has(uint32_t x) const { return x >= lo && x <= hi && (bin < 0 || map(x) == bin); }
 };
 
 template <int NT, int KPT>
@@ -361,19 +490,23 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
   constexpr int NW = NT / 64;
   constexpr int BPT = kBins / NT;                   // histogram bins per thread in the scan
   constexpr int TAB = KPT > 0 ? NW * KPT : 1;       // per-(round, wavefront) table
+  constexpr bool kKeepBins = KPT > 0 && KPT <= 16;  // first-pass bins kept in registers (16 bits each)
   static_assert(TAB <= 512, "table scan covers at most 512 entries");
-  __shared__ uint32_t hist2[2][kBins];  // alternating pass histograms
+  static_assert(KPT <= 64, "member mask holds one bit per round");
+  __shared__ uint32_t hist2[2][kBins + 1];  // alternating pass histograms; the last slot takes non-members
   __shared__ int lds_waves[NW];
-  __shared__ uint32_t lds_and[NW], lds_or[NW];
+  __shared__ uint32_t lds_min[NW], lds_max[NW];
   __shared__ uint32_t bucket[kFinishMax];
   __shared__ int tab[TAB];
-  __shared__ int bc[4];
+  __shared__ int bc[3];
 
   const int i = blockIdx.x;
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  KeyRuns<NT, KPT> kr;
+  kr.prefetch(keys + ((size_t)r * H + i) * max_blocks, max_blocks);  // in flight with seq_lens
   const int L = clampi(seq_lens[r], 0, max_blocks * kBlock);
   const int M = (L + kBlock - 1) / kBlock;
   int32_t* out = sel_idx + ((size_t)r * H + i) * max_sel;
@@ -400,59 +533,70 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     return;
   }
 
-  KeyRuns<NT, KPT> kr;
-  kr.load(keys + ((size_t)r * H + i) * max_blocks, C);
+  kr.set_count(C);
   const int R = kr.nrounds();
-  for (int b = tid; b < kBins; b += NT) hist2[0][b] = 0u;  // published by the next barrier
-  if (tid == 0) bc[3] = 0;
+  for (int b = tid; b <= kBins; b += NT) hist2[0][b] = 0u;  // published by the next barrier
 
-  // Bits shared by every candidate key.
-  uint32_t a = 0xffffffffu, o = 0u;
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const bool v = kr.valid(j);
+  // Key range of all candidates.
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  RESA_FOR_KEYS({
     const uint32_t x = kr.key(j);
-    a &= v ? x : 0xffffffffu;
-    o |= v ? x : 0u;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    a &= (uint32_t)__shfl_xor((int)a, off);
-    o |= (uint32_t)__shfl_xor((int)o, off);
-  }
-  if (lane == 0) {
-    lds_and[wave] = a;
-    lds_or[wave] = o;
-  }
-  __syncthreads();
-  a = 0xffffffffu;
-  o = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    a &= lds_and[w];
-    o |= lds_or[w];
-  }
-  const uint32_t diff = a ^ o;
-  int top = diff ? 31 - __clz(diff) : -1;  // highest bit in which candidates differ
-  uint32_t fixed = top >= 31 ? 0u : (top < 0 ? 0xffffffffu : ~((2u << top) - 1u));
-  uint32_t prefix = a & fixed;
-  int remaining = k;   // keys still to take among those whose fixed bits equal `prefix`
-  int bucket_n = C;    // keys whose fixed bits equal `prefix`
+    mn = in ? min(mn, x) : mn;
+    mx = in ? max(mx, x) : mx;
+  });
+  block_min_max<NT>(mn, mx, lds_min, lds_max);
 
-  // Histogram passes over 11-bit digits until the boundary bucket is small.
+  Bucket bk;
+  bk.lo = mn;
+  bk.hi = mx;
+  bk.bin = -1;
+  bk.map.init(mn, mx, false);
+  int remaining = k;  // keys still to take from the bucket
+  int bucket_n = C;   // keys in the bucket
+  uint32_t bins[kKeepBins ? KPT / 2 : 1];  // first-pass bin of every key, two per register
+
+  // Histogram passes until the bucket holding the k-th largest key is small.
   int npass = 0;
-  while (top >= 0 && bucket_n > kFinishMax && remaining != bucket_n) {
-    const int width = top + 1 < kDigitBits ? top + 1 : kDigitBits;
-    const int shift = top + 1 - width;
-    const uint32_t dmask = (1u << width) - 1u;
+  while (bucket_n > kFinishMax && remaining < bucket_n && bk.lo != bk.hi) {
+    if (bk.bin >= 0) {  // re-measure the range of the previous pass's bucket
+      uint32_t a = 0xffffffffu, b = 0u;
+      RESA_FOR_KEYS({
+        const uint32_t x = kr.key(j);
+        const bool m = in && bk.has(x);
+        a = m ? min(a, x) : a;
+        b = m ? max(b, x) : b;
+      });
+      block_min_max<NT>(a, b, lds_min, lds_max);
+      bk.lo = a;
+      bk.hi = b;
+      bk.bin = -1;
+      if (a == b) break;
+    }
+    BinMap map;
+    map.init(bk.lo, bk.hi, npass == 0);
     uint32_t* hist = hist2[npass & 1];
     uint32_t* hist_next = hist2[(npass + 1) & 1];
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const uint32_t x = kr.key(j);
-      if (kr.valid(j) && (x & fixed) == prefix) atomicAdd(&hist[(x >> shift) & dmask], 1u);
+    if (npass == 0) {  // every candidate is in the bucket
+#define RESA_COUNT_KEY(BIN)                                         \
+  {                                                                 \
+    const int b = BIN;                                              \
+    if (in) atomicAdd(&hist[b], 1u);                                \
+    if constexpr (kKeepBins) {                                      \
+      const uint32_t kept = in ? (uint32_t)b : (uint32_t)kBins;     \
+      if (j & 1) bins[j / 2] |= kept << 16;                         \
+      else bins[j / 2] = kept;                                      \
+    }                                                               \
+  }
+      if (map.by_value) RESA_FOR_KEYS(RESA_COUNT_KEY(map.value_bin(kr.key(j))));
+      else RESA_FOR_KEYS(RESA_COUNT_KEY(map.key_bin(kr.key(j))));
+#undef RESA_COUNT_KEY
+    } else {
+      RESA_FOR_KEYS({
+        const uint32_t x = kr.key(j);
+        if (in && bk.has(x)) atomicAdd(&hist[map(x)], 1u);
+      });
     }
-    for (int b = tid; b < kBins; b += NT) hist_next[b] = 0u;  // next pass's histogram
+    for (int b = tid; b <= kBins; b += NT) hist_next[b] = 0u;  // next pass's histogram
     __syncthreads();
     // Suffix counts: thread t owns bins [BPT*rt, BPT*rt + BPT) with rt = NT-1-t,
     // so an exclusive scan in thread order counts the keys in higher bins.
@@ -479,85 +623,101 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
       }
     }
     __syncthreads();
-    prefix |= (uint32_t)bc[0] << shift;
-    fixed |= dmask << shift;
+    bk.map = map;
+    bk.bin = bc[0];
     remaining = bc[1];
     bucket_n = bc[2];
-    top = shift - 1;
     ++npass;
     __syncthreads();
   }
 
-  // Single-wavefront finish: the boundary bucket (<= 256 keys) goes to LDS and
-  // one wavefront resolves the remaining bits one at a time with ballots.
-  if (top >= 0 && remaining != bucket_n) {
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const uint32_t x = kr.key(j);
-      const bool in_b = kr.valid(j) && (x & fixed) == prefix;
-      const unsigned long long m = __ballot(in_b);
-      if (m) {  // one LDS atomic per wavefront and round
-        int base = 0;
-        if (lane == 0) base = atomicAdd(&bc[3], __popcll(m));
-        base = __shfl(base, 0);
-        if (in_b) bucket[base + (int)lane_prefix(m)] = x;
+  // The threshold: the remaining-th largest key of the bucket.  Keys above it
+  // are taken; of the n_eq keys equal to it, the `take_eq` lowest block ids.
+  uint32_t thr;
+  int take_eq, n_eq;
+  if (bk.lo == bk.hi) {  // every key in the bucket is equal
+    thr = bk.lo;
+    take_eq = remaining;
+    n_eq = bucket_n;
+  } else if (bucket_n <= kFinishMax) {
+    // Ranking finish: the bucket's keys are packed into LDS (offsets from a
+    // scan of per-thread member counts), then each member counts the members
+    // above and equal to it; the one whose rank range holds `remaining` is
+    // the threshold.
+    unsigned long long mask = 0;  // KPT > 0: member bit per round
+    int cnt = 0;
+    const bool kept = kKeepBins && npass == 1;
+    RESA_FOR_KEYS({
+      bool m;
+      if constexpr (kKeepBins) {
+        if (kept) m = (int)((bins[j / 2] >> (16 * (j & 1))) & 0xffffu) == bk.bin;  // non-candidates kept kBins
+        else m = in && bk.has(kr.key(j));
+      } else {
+        m = in && bk.has(kr.key(j));
       }
-    }
+      if constexpr (KPT > 0) mask |= (m ? 1ull : 0ull) << j;
+      cnt += m ? 1 : 0;
+    });
+    int tot;
+    int pos = block_exclusive_scan<NT>(cnt, lds_waves, tot);
+    RESA_FOR_KEYS({
+      bool m;
+      if constexpr (KPT > 0) m = (mask >> j) & 1ull;
+      else m = in && bk.has(kr.key(j));
+      if (m) {
+        if (pos < kFinishMax) bucket[pos] = kr.key(j);
+        ++pos;
+      }
+    });
     __syncthreads();
-    if (wave == 0) {
-      uint32_t v[kFinishMax / 64];
-      bool in[kFinishMax / 64];
-#pragma unroll
-      for (int e = 0; e < kFinishMax / 64; ++e) {
-        const int idx = lane + 64 * e;
-        in[e] = idx < bucket_n;
-        v[e] = in[e] ? bucket[idx] : 0u;
+    const int nb = tot < kFinishMax ? tot : kFinishMax;
+    if (tid < nb) {
+      const uint32_t x = bucket[tid];
+      int gt = 0, eq = 0;
+      for (int q = 0; q < nb; ++q) {
+        const uint32_t y = bucket[q];
+        gt += y > x ? 1 : 0;
+        eq += y == x ? 1 : 0;
       }
-      int rem = remaining;
-      uint32_t pre = prefix, fx = fixed;
-      for (int bit = top; bit >= 0; --bit) {
-        const uint32_t bm = 1u << bit;
-        int ones = 0;
-#pragma unroll
-        for (int e = 0; e < kFinishMax / 64; ++e)
-          ones += __popcll(__ballot(in[e] && (v[e] & fx) == pre && (v[e] & bm)));
-        if (ones >= rem) {
-          pre |= bm;
-        } else {
-          rem -= ones;
-        }
-        fx |= bm;
-      }
-      int eq = 0;
-#pragma unroll
-      for (int e = 0; e < kFinishMax / 64; ++e) eq += __popcll(__ballot(in[e] && v[e] == pre));
-      if (lane == 0) {
-        bc[0] = (int)pre;
-        bc[1] = rem;
+      if (gt < remaining && remaining <= gt + eq) {  // every writer stores the same values
+        bc[0] = (int)x;
+        bc[1] = remaining - gt;
         bc[2] = eq;
       }
     }
     __syncthreads();
-    prefix = (uint32_t)bc[0];
-    fixed = 0xffffffffu;
-    remaining = bc[1];
-    bucket_n = bc[2];
+    thr = (uint32_t)bc[0];
+    take_eq = bc[1];
+    n_eq = bc[2];
+  } else {
+    // remaining == bucket_n: the whole bucket is taken; the threshold is its
+    // smallest key and every key equal to it lies in the bucket.
+    uint32_t a = 0xffffffffu, b = 0u;
+    RESA_FOR_KEYS({
+      const uint32_t x = kr.key(j);
+      a = (in && bk.has(x)) ? min(a, x) : a;
+    });
+    block_min_max<NT>(a, b, lds_min, lds_max);
+    thr = a;
+    take_eq = bucket_n;
+    n_eq = bucket_n;
   }
 
-  // Output in ascending block order.  Keys whose fixed bits exceed `prefix`
-  // are taken; of the bucket_n keys equal to it, the `remaining` lowest ids.
-  // Round j of wavefront w covers blocks [NT j + 64 w, NT j + 64 w + 64), so a
-  // table of per-(round, wavefront) ballot counts, scanned once, gives every
-  // wavefront's output offset and a lane prefix count places each block.
-  const bool ties = remaining < bucket_n;
+  // Output in ascending block order.  Round j of wavefront w covers blocks
+  // [NT j + 64 w, NT j + 64 w + 64), so a table of per-(round, wavefront)
+  // ballot counts, scanned once, gives every wavefront's output offset and a
+  // lane prefix count places each block.
+  const bool ties = take_eq < n_eq;
   if constexpr (KPT > 0) {
     int eq_rank_base[KPT];
     if (ties) {
+      int counts = 0;
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        const unsigned long long m = __ballot(kr.valid(j) && (kr.key(j) & fixed) == prefix);
-        if (lane == 0) tab[j * NW + wave] = __popcll(m);
+        const int c = __popcll(__ballot(kr.valid(j) && kr.key(j) == thr));
+        counts = lane == j ? c : counts;
       }
+      if (lane < KPT) tab[lane * NW + wave] = counts;
       __syncthreads();
       if (wave == 0) wave_scan_table(tab, TAB);
       __syncthreads();
@@ -567,21 +727,24 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     }
     bool take[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) take[j] = kr.valid(j) && (kr.key(j) & fixed) >= prefix;
+    for (int j = 0; j < KPT; ++j) take[j] = false;
+    RESA_FOR_KEYS({ take[j] = in && kr.key(j) >= thr; });
     if (ties) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        const bool is_eq = kr.valid(j) && (kr.key(j) & fixed) == prefix;
+        const bool is_eq = kr.valid(j) && kr.key(j) == thr;
         const unsigned long long m = __ballot(is_eq);
         const int rank = eq_rank_base[j] + (int)lane_prefix(m);
-        if (is_eq) take[j] = rank < remaining;
+        if (is_eq) take[j] = rank < take_eq;
       }
     }
+    int counts = 0;  // lane j: this wavefront's count in round j
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const unsigned long long m = __ballot(take[j]);
-      if (lane == 0) tab[j * NW + wave] = __popcll(m);
+      const int c = __popcll(__ballot(take[j]));  // ballot outside the lane select
+      counts = lane == j ? c : counts;
     }
+    if (lane < KPT) tab[lane * NW + wave] = counts;
     __syncthreads();
     if (wave == 0) wave_scan_table(tab, TAB);
     __syncthreads();
@@ -596,11 +759,11 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     int base_out = 0, base_eq = 0;
     for (int j = 0; j < R; ++j) {
       const bool v = kr.valid(j);
-      const uint32_t x = kr.key(j) & fixed;
-      const bool is_eq = v && x == prefix;
+      const uint32_t x = kr.key(j);
+      const bool is_eq = v && x == thr;
       int tot_eq;
       const int eq_before = block_exclusive_scan<NT>(is_eq ? 1 : 0, lds_waves, tot_eq);
-      const bool t = (v && x > prefix) || (is_eq && (!ties || base_eq + eq_before < remaining));
+      const bool t = (v && x > thr) || (is_eq && (!ties || base_eq + eq_before < take_eq));
       int tot;
       const int pos = block_exclusive_scan<NT>(t ? 1 : 0, lds_waves, tot);
       if (t && base_out + pos < k) out[base_out + pos] = tid + j * NT;
