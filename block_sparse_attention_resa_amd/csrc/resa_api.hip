@@ -79,7 +79,15 @@ int splits_for(const resa_config* c, int op, int R, int max_blocks, int max_sel,
     len = max_blocks;
     target = 256;
     min_share = 8 * kDecodeWaves;
-  } else {  // rectify
+  } else if (c->dtype == RESA_BF16) {  // rectify, 256 query rows per workgroup: about one per CU
+    const long long rg = ceil_div((long long)chunk * c->group_size, 256);
+    len = max_blocks;
+    target = 256 / (rg > 0 ? rg : 1);
+    min_share = 32;
+    // a split keeps the physical ids of its blocks in LDS: at most 2048 of them
+    const long long units_all = units > 0 ? units : 1;
+    if (target < units_all * ceil_div(max_blocks, 2048)) target = units_all * ceil_div(max_blocks, 2048);
+  } else {  // rectify, fp32: 64 query rows per workgroup
     const long long rg = ceil_div((long long)chunk * c->group_size, 64);
     len = max_blocks;
     target = 1024 / (rg > 0 ? rg : 1);
