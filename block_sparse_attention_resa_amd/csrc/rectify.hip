@@ -235,15 +235,16 @@ struct RectLds {
 };
 
 // One 16-byte piece per lane from global memory straight into LDS at
-// lds_wave + 16 * lane (lds_wave must be the same for the whole wavefront).
+// lds_wave + 16 * lane (lds_wave is the same for the whole wavefront).  The
+// copy is written out so that the compiler does not track it: it would
+// otherwise wait for every copy in flight before any LDS read from a stage
+// it cannot tell apart.  The instruction writes no register; its completion
+// is awaited explicitly (vmcnt in ring_sync) before the stage is read.
 __device__ __forceinline__ void copy_to_lds16(const bf16_t* src, bf16_t* lds_wave) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (__attribute__((address_space(3))) void*)lds_wave,
-                                   16, 0, 0);
-#else
-  (void)src;
-  (void)lds_wave;
-#endif
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)lds_wave);  // LDS byte offset
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
+               : "memory", "m0");
 }
 
 // Maximum over the four lanes of a score-tile column (lanes l, l ^ 16,
@@ -325,6 +326,17 @@ __global__ __launch_bounds__(kRlThreads) void rectify_attn_lds_kernel(
       qf[c][kk] = ok ? *reinterpret_cast<const uint4*>(qrow + quad * 8 * KK + 8 * kk) : make_uint4(0, 0, 0, 0);
   }
 
+  // The query fragments are complete before the loop: the compiler does not
+  // track the LDS copies, and a load of its own still pending inside the loop
+  // would make it wait for every copy in flight there.
+#pragma unroll
+  for (int c = 0; c < kRlTiles; ++c)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint4 x = qf[c][kk];
+      asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
+    }
+
   float m_ref[kRlTiles], l_run[kRlTiles];
   floatx4_t acc[kRlTiles][NT];
 #pragma unroll
@@ -398,7 +410,34 @@ __global__ __launch_bounds__(kRlThreads) void rectify_attn_lds_kernel(
         sv[b][c] = x;
       }
     }
-    uint4 ph[kRlTiles], pl[kRlTiles];
+    // Value operands of both blocks, shared by every tile: V^T slots 0-3 are
+    // block 0 tokens 4q..4q+3, slots 4-7 block 1.  Entries of blocks past the
+    // split and of tokens past the sequence end are zeroed: their
+    // probability is 0 but the bytes there may be anything.
+    bf16x8_t vop[NT];
+    {
+      uint2 keep[kRlStep];
+#pragma unroll
+      for (int b = 0; b < kRlStep; ++b) {
+        if constexpr (decltype(masked)::value) {
+          const int vl = blk0 + b < end ? L - (blk0 + b) * kBlock - 4 * quad : 0;  // valid tokens from 4q on
+          keep[b].x = (vl > 0 ? 0xffffu : 0u) | (vl > 1 ? 0xffff0000u : 0u);
+          keep[b].y = (vl > 2 ? 0xffffu : 0u) | (vl > 3 ? 0xffff0000u : 0u);
+        } else {
+          keep[b] = make_uint2(0xffffffffu, 0xffffffffu);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        uint2 v0 = *reinterpret_cast<const uint2*>(vb + (16 * t + col) * kBlock + 4 * quad);
+        uint2 v1 = *reinterpret_cast<const uint2*>(vb + LY::BLK + (16 * t + col) * kBlock + 4 * quad);
+        if constexpr (decltype(masked)::value) {
+          v0 = make_uint2(v0.x & keep[0].x, v0.y & keep[0].y);
+          v1 = make_uint2(v1.x & keep[1].x, v1.y & keep[1].y);
+        }
+        vop[t] = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+      }
+    }
 #pragma unroll
     for (int c = 0; c < kRlTiles; ++c) {
       float mx = -INFINITY;
@@ -434,8 +473,8 @@ __global__ __launch_bounds__(kRlThreads) void rectify_attn_lds_kernel(
           p[4 * b + e] = __builtin_amdgcn_exp2f(fmaf(sv[b][c][e], scale_log2, neg_m));
           l_run[c] += p[4 * b + e];
         }
-      // P^T operands (slots 0-3 block 0 tokens 4q..4q+3, slots 4-7 block 1):
-      // a bf16 high part and the bf16 of the residual
+      // P^T operands, same slot order as V^T: a bf16 high part and the bf16
+      // of the residual
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
@@ -445,79 +484,48 @@ __global__ __launch_bounds__(kRlThreads) void rectify_attn_lds_kernel(
         hw[h] = __builtin_bit_cast(uint32_t, hi);
         lw[h] = __builtin_bit_cast(uint32_t, lo);
       }
-      ph[c] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      pl[c] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-    }
-    // Value entries of blocks past the split and of tokens past the sequence
-    // end are zeroed: their probability is 0 but the bytes may be anything.
-    uint2 keep[kRlStep];
+      const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      // O^T += V^T . P^T over both blocks
 #pragma unroll
-    for (int b = 0; b < kRlStep; ++b) {
-      if constexpr (decltype(masked)::value) {
-        const int vl = blk0 + b < end ? L - (blk0 + b) * kBlock - 4 * quad : 0;  // valid tokens from 4q on
-        keep[b].x = (vl > 0 ? 0xffffu : 0u) | (vl > 1 ? 0xffff0000u : 0u);
-        keep[b].y = (vl > 2 ? 0xffffu : 0u) | (vl > 3 ? 0xffff0000u : 0u);
-      } else {
-        keep[b] = make_uint2(0xffffffffu, 0xffffffffu);
-      }
-    }
-    // O^T += V^T . P^T over both blocks
+      for (int t = 0; t < NT; ++t) acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[t], ph, acc[c][t], 0, 0, 0);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      uint2 v0 = *reinterpret_cast<const uint2*>(vb + (16 * t + col) * kBlock + 4 * quad);
-      uint2 v1 = *reinterpret_cast<const uint2*>(vb + LY::BLK + (16 * t + col) * kBlock + 4 * quad);
-      if constexpr (decltype(masked)::value) {
-        v0 = make_uint2(v0.x & keep[0].x, v0.y & keep[0].y);
-        v1 = make_uint2(v1.x & keep[1].x, v1.y & keep[1].y);
-      }
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
-#pragma unroll
-      for (int c = 0; c < kRlTiles; ++c)
-        acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, ph[c]), acc[c][t], 0, 0, 0);
-#pragma unroll
-      for (int c = 0; c < kRlTiles; ++c)
-        acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, pl[c]), acc[c][t], 0, 0, 0);
+      for (int t = 0; t < NT; ++t) acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[t], pl, acc[c][t], 0, 0, 0);
     }
   };
 
   // Steps go in pairs, one barrier per pair: pair (s, s + 1) is computed
   // from stages s % NS and (s + 1) % NS while the copies of the next
   // NS - 2 steps are in flight; after the barrier the two stages of the
-  // previous pair are free and receive steps s + NS - 2 and s + NS - 1.  The
-  // pair loop is unrolled NS / 2 times so that every stage index is a
-  // constant, which lets the compiler see that the LDS reads of a stage do
-  // not overlap the copies in flight into the others.
+  // previous pair are free and receive steps s + NS - 2 and s + NS - 1.
   static_assert(NS % 2 == 0 && NS >= 4, "stages come in pairs");
 #pragma unroll
   for (int j = 0; j < NS - 2; ++j)
     if (j < nsteps) issue(j, j);
+  int stage = 0;
 #pragma clang loop unroll(disable)
-  for (int s0 = 0; s0 < nsteps; s0 += NS) {
+  for (int step = 0; step < nsteps; step += 2) {
+    // this pair's copies are done once at most the next pair's are pending
+    if (step + NS - 3 < nsteps) ring_sync<LY::ISSUES * 2>();
+    else ring_sync<0>();
+    const int freed = stage == 0 ? NS - 2 : stage - 2;  // stages of the previous pair
+    if (step + NS - 2 < nsteps) issue(step + NS - 2, freed);
+    if (step + NS - 1 < nsteps) issue(step + NS - 1, freed + 1);
 #pragma unroll
-    for (int u = 0; u < NS; u += 2) {
-      const int step = s0 + u;
-      if (step < nsteps) {
-        // this pair's copies are done once at most the next pair's are pending
-        if (step + NS - 3 < nsteps) ring_sync<LY::ISSUES * 2>();
-        else ring_sync<0>();
-        const int freed = (u + NS - 2) % NS;  // stages of the previous pair
-        if (step + NS - 2 < nsteps) issue(step + NS - 2, freed);
-        if (step + NS - 1 < nsteps) issue(step + NS - 1, freed + 1);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const bf16_t* kb = lds + (u + h) * LY::STAGE;
-          const bf16_t* vb = kb + kRlStep * LY::BLK;
-          const int blk0 = beg + (step + h) * kRlStep;
-          // Steps wholly inside the split, the sequence and every row's causal
-          // window (all but the last few) skip the masking.
-          const bool plain = blk0 + kRlStep <= end && (blk0 + kRlStep) * kBlock - 1 <= lim_lo;
-          if (plain) compute(kb, vb, blk0, std::integral_constant<bool, false>{});
-          else compute(kb, vb, blk0, std::integral_constant<bool, true>{});
-          __builtin_amdgcn_sched_barrier(0);  // keep the steps' live ranges apart
-        }
-      }
+    for (int h = 0; h < 2; ++h) {
+      const bf16_t* kb = lds + (stage + h) * LY::STAGE;
+      const bf16_t* vb = kb + kRlStep * LY::BLK;
+      const int blk0 = beg + (step + h) * kRlStep;
+      // Steps wholly inside the split, the sequence and every row's causal
+      // window (all but the last few) skip the masking.
+      const bool plain = blk0 + kRlStep <= end && (blk0 + kRlStep) * kBlock - 1 <= lim_lo;
+      if (plain) compute(kb, vb, blk0, std::integral_constant<bool, false>{});
+      else compute(kb, vb, blk0, std::integral_constant<bool, true>{});
+      __builtin_amdgcn_sched_barrier(0);  // keep the two steps' live ranges apart
     }
+    stage = stage == NS - 2 ? 0 : stage + 2;
   }
+  ring_sync<0>();  // no copy may still be writing when the workgroup ends
 
 #pragma unroll
   for (int c = 0; c < kRlTiles; ++c) {
