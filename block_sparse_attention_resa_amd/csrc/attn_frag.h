@@ -23,6 +23,22 @@
 
 namespace resa {
 
+typedef __attribute__((ext_vector_type(2))) float float2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+
+// Maximum over the four lanes of a score-tile column (lanes l, l ^ 16,
+// l ^ 32, l ^ 48) with the lane-swap instructions: after a swap of the two
+// 32-lane halves (then of neighbouring 16-lane rows) between two copies of
+// the value, each lane holds its own value in one copy and its partner's in
+// the other.
+__device__ __forceinline__ float quad_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <typename T, int D>
 struct Frag;
 
@@ -77,14 +93,17 @@ struct Frag<bf16_t, D> {
     }
   }
   __device__ static void pv(floatx4_t* acc, const KV& f, const float* p) {
-    uint32_t hi[4], lo[4];
+    uint32_t hw[2], lw[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      hi[e] = f32_to_bf16_bits(p[e]);
-      lo[e] = f32_to_bf16_bits(p[e] - __uint_as_float(hi[e] << 16));
+    for (int h = 0; h < 2; ++h) {  // bf16 high parts and the bf16 of the residuals, two per instruction
+      const bf16x2_t hi = __builtin_convertvector(float2_t{p[2 * h], p[2 * h + 1]}, bf16x2_t);
+      const float2_t hf = __builtin_convertvector(hi, float2_t);
+      const bf16x2_t lo = __builtin_convertvector(float2_t{p[2 * h] - hf.x, p[2 * h + 1] - hf.y}, bf16x2_t);
+      hw[h] = __builtin_bit_cast(uint32_t, hi);
+      lw[h] = __builtin_bit_cast(uint32_t, lo);
     }
-    const uint2 ph = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-    const uint2 pl = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+    const uint2 ph = make_uint2(hw[0], hw[1]);
+    const uint2 pl = make_uint2(lw[0], lw[1]);
     const short4_t bh = __builtin_bit_cast(short4_t, ph);
     const short4_t bl = __builtin_bit_cast(short4_t, pl);
 #pragma unroll

@@ -161,13 +161,12 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(
           sv[j] = floatx4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = quad_max(mx);
       const float m_new = fmaxf(m_run, mx);
       // With nothing valid seen yet (m_new = -inf) keep the state unchanged;
       // otherwise alpha = 0 on the first chunk (m_run = -inf).
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -178,7 +177,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(
           float p[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            p[e] = exp2f(sv[j][e] - m_use);
+            p[e] = __builtin_amdgcn_exp2f(sv[j][e] - m_use);
             l_run += p[e];
           }
           F::pv(acc, c.f[j], p);
@@ -241,100 +240,90 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(
 
 }
 
-// Log-sum-exp merge of split partials.  One workgroup per output row:
+// Log-sum-exp merge of split partials:
 //   out[c] = sum_s 2^(m_s - m) o_s[c] / sum_s 2^(m_s - m) l_s,  m = max_s m_s.
-// Every load of a batch (the row's m_s, l_s and the partial outputs) is issued
-// before the first reduction, so a batch of up to kMergeBatch splits costs one
-// memory round trip.  Thread (g, c4) sums splits g, g + NG, ... of channel
-// quad c4 in increasing order; the NG group sums are added in group order, so
-// the result is deterministic.
+// Four consecutive lanes share one output float4: lane part p folds splits
+// p, p + 4, p + 8, ... in increasing order with the running (m, l, o) update,
+// all loads of a batch of kMergeBatch splits issued before the first use;
+// the four partial states are then combined (parts 0+1, 2+3, then both) by
+// lane exchanges.  No barrier and no LDS, and the order of every sum is
+// fixed, so the result is deterministic.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeBatch = 16;  // splits per thread held in registers per batch
+constexpr int kMergeParts = 16;  // lanes per output float4
+constexpr int kMergeBatch = 4;   // splits per lane per batch of loads
 
-__device__ __forceinline__ float block_reduce(float v, float* lds, bool is_max) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float o = __shfl_xor(v, off);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  if (lane == 0) lds[wave] = v;
-  __syncthreads();
-  float r = lds[0];
-#pragma unroll
-  for (int w = 1; w < kMergeThreads / 64; ++w) r = is_max ? fmaxf(r, lds[w]) : r + lds[w];
-  __syncthreads();
-  return r;
+struct MergeState {
+  float m, l;
+  floatx4_t o;
+};
+
+__device__ __forceinline__ void merge_into(MergeState& a, float m_s, float l_s, floatx4_t o_s) {
+  const float m = fmaxf(a.m, m_s);
+  if (m == -INFINITY) return;  // nothing seen on either side
+  const float wa = a.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(a.m - m);
+  const float wb = m_s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_s - m);
+  a.l = a.l * wa + l_s * wb;
+  a.o = a.o * wa + o_s * wb;
+  a.m = m;
 }
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part_o,
                                                               const float* __restrict__ part_ml,
                                                               float* __restrict__ out, int H, int G, int S,
-                                                              int rows_per_head, int row_stride_out) {
-  constexpr int C4 = D / 4;               // float4 lanes per row
-  constexpr int NG = kMergeThreads / C4;  // split groups
-  __shared__ float s_w[kMaxSplits];
-  __shared__ float s_red[kMergeThreads / 64];
-  __shared__ floatx4_t s_acc[kMergeThreads];
-  const int row = blockIdx.x;
-  const int i = blockIdx.y;
-  const int r = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int c4 = tid % C4;
-  const int grp = tid / C4;
-  const size_t base = ((size_t)r * H + i) * S;
+                                                              int rows_per_head, int row_stride_out,
+                                                              int total_rows) {
+  constexpr int C4 = D / 4;  // float4 per output row
+  const int g = blockIdx.x * kMergeThreads + threadIdx.x;
+  const int part = g % kMergeParts;
+  const int c4 = (g / kMergeParts) % C4;
+  const int grow = g / (kMergeParts * C4);  // (r, i, row) flattened
+  const bool live = grow < total_rows;
+  const int row = live ? grow % rows_per_head : 0;
+  const int ri = live ? grow / rows_per_head : 0;  // r * H + i
+  const size_t base = (size_t)ri * S;
 
-  float mv[kMaxSplits / kMergeThreads], lv[kMaxSplits / kMergeThreads];
+  MergeState st{-INFINITY, 0.f, floatx4_t{0.f, 0.f, 0.f, 0.f}};
+  for (int s0 = part; s0 < S; s0 += kMergeParts * kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch];
+    floatx4_t ov[kMergeBatch];
 #pragma unroll
-  for (int k = 0; k < kMaxSplits / kMergeThreads; ++k) {
-    const int s = tid + k * kMergeThreads;
-    const size_t pr = (base + (s < S ? s : 0)) * rows_per_head + row;
-    mv[k] = s < S ? part_ml[pr * 2] : -INFINITY;
-    lv[k] = s < S ? part_ml[pr * 2 + 1] : 0.f;
+    for (int b = 0; b < kMergeBatch; ++b) {
+      const int sp = s0 + b * kMergeParts;
+      const bool ok = live && sp < S;
+      const size_t pr = (base + (ok ? sp : 0)) * rows_per_head + row;
+      const float2 ml = *reinterpret_cast<const float2*>(part_ml + pr * 2);
+      mv[b] = ok ? ml.x : -INFINITY;
+      lv[b] = ok ? ml.y : 0.f;
+      ov[b] = *reinterpret_cast<const floatx4_t*>(part_o + pr * D + 4 * c4);
+    }
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) merge_into(st, mv[b], lv[b], ov[b]);
   }
-  floatx4_t ov[kMergeBatch];
+  // combine the four parts: xor 1 then xor 2 (lanes of one output are consecutive)
 #pragma unroll
-  for (int b = 0; b < kMergeBatch; ++b) {
-    const int s = grp + b * NG;
-    ov[b] = s < S ? *reinterpret_cast<const floatx4_t*>(part_o + ((base + s) * rows_per_head + row) * D + 4 * c4)
-                  : floatx4_t{0.f, 0.f, 0.f, 0.f};
+  for (int off = 1; off < kMergeParts; off <<= 1) {
+    const float m_o = __shfl_xor(st.m, off);
+    const float l_o = __shfl_xor(st.l, off);
+    floatx4_t o_o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o_o[e] = __shfl_xor(st.o[e], off);
+    if ((part & off) == 0) {
+      merge_into(st, m_o, l_o, o_o);
+    } else {  // the same sum in the same order as the partner computes it
+      MergeState other{m_o, l_o, o_o};
+      merge_into(other, st.m, st.l, st.o);
+      st = other;
+    }
   }
-
-  float m = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kMaxSplits / kMergeThreads; ++k) m = fmaxf(m, mv[k]);
-  m = block_reduce(m, s_red, true);
-  float den = 0.f;
-#pragma unroll
-  for (int k = 0; k < kMaxSplits / kMergeThreads; ++k) {
-    const int s = tid + k * kMergeThreads;
-    const float w = (m == -INFINITY || mv[k] == -INFINITY) ? 0.f : exp2f(mv[k] - m);
-    if (s < S) s_w[s] = w;
-    den += w * lv[k];
-  }
-  den = block_reduce(den, s_red, false);  // its barriers also publish s_w
-
-  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int b = 0; b < kMergeBatch; ++b) {
-    const int s = grp + b * NG;
-    if (s < S) acc += s_w[s] * ov[b];
-  }
-  for (int s = grp + kMergeBatch * NG; s < S; s += NG)  // splits beyond one batch (large S)
-    acc += s_w[s] * *reinterpret_cast<const floatx4_t*>(part_o + ((base + s) * rows_per_head + row) * D + 4 * c4);
-  s_acc[tid] = acc;
-  __syncthreads();
-  if (grp == 0) {
-    floatx4_t sum = acc;
-#pragma unroll
-    for (int gi = 1; gi < NG; ++gi) sum += s_acc[gi * C4 + c4];
+  if (live && part == 0) {
+    const int r = ri / H;
+    const int i = ri % H;
     const int j = row % G;
     const int t = row / G;
     float* dst = out + (((size_t)r * row_stride_out + t) * H * G + (size_t)i * G + j) * D + 4 * c4;
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    *reinterpret_cast<floatx4_t*>(dst) = sum * inv;
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    *reinterpret_cast<floatx4_t*>(dst) = st.o * inv;
   }
 }
 
@@ -362,13 +351,15 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_merge(const float* part_o, const float* part_ml, float* out, int R, int H, int G, int D, int S,
                         int rows_per_head, int row_stride_out, hipStream_t stream) {
-  const dim3 grid((unsigned)rows_per_head, (unsigned)H, (unsigned)R);
+  const long long rows = (long long)R * H * rows_per_head;
+  const long long threads = rows * (D / 4) * kMergeParts;
+  const dim3 grid((unsigned)((threads + kMergeThreads - 1) / kMergeThreads));
   if (D == 128)
     hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(kMergeThreads), 0, stream, part_o, part_ml, out, H, G, S,
-                       rows_per_head, row_stride_out);
+                       rows_per_head, row_stride_out, (int)rows);
   else
     hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(kMergeThreads), 0, stream, part_o, part_ml, out, H, G, S,
-                       rows_per_head, row_stride_out);
+                       rows_per_head, row_stride_out, (int)rows);
   return hipGetLastError();
 }
 

@@ -209,9 +209,6 @@ __global__ __launch_bounds__(kRectThreads) void rectify_attn_kernel(
 // both operands.  P enters as a bf16 high part and a bf16 residual, as in
 // decode.  Key rows are stored with their 16-byte pieces XOR-swizzled by row
 // so the sixteen rows a wavefront reads together fall in different banks.
-typedef __attribute__((ext_vector_type(2))) float float2_t;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-
 constexpr int kRlWaves = 8;
 constexpr int kRlThreads = 64 * kRlWaves;
 constexpr int kRlTiles = 2;                         // 16-column tiles per wavefront
@@ -245,18 +242,6 @@ __device__ __forceinline__ void copy_to_lds16(const bf16_t* src, bf16_t* lds_wav
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)lds_wave);  // LDS byte offset
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
                : "memory", "m0");
-}
-
-// Maximum over the four lanes of a score-tile column (lanes l, l ^ 16,
-// l ^ 32, l ^ 48) with the lane-swap instructions: after a swap of the two
-// 32-lane halves (then of neighbouring 16-lane rows) between two copies of
-// the value, each lane holds its own value in one copy and its partner's in
-// the other.
-__device__ __forceinline__ float quad_max(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // vmcnt(N) together with lgkmcnt(0), then a workgroup barrier.  The LDS

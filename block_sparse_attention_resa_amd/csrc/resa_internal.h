@@ -10,7 +10,7 @@
 namespace resa {
 
 constexpr int kBlock = 16;       // tokens per KV block
-constexpr int kMaxSplits = 1024;  // split partials one merge workgroup combines
+constexpr int kMaxSplits = 1024;  // upper bound on the split count of one call
 constexpr int kDecodeWaves = 8;   // wavefronts per decode workgroup
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
