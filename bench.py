@@ -92,6 +92,8 @@ def main(argv=None):
                     help="skip the CPU oracle leg (for profiler runs)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (HBM counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line: context x budget x scoring-mode table (markdown)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -110,6 +112,8 @@ def main(argv=None):
         return 2
     resa.load_library()
     torch.cuda.set_device(0)
+    if args.sweep:
+        return sweep(args)
     spec = WORKLOADS[args.workload]
     assert spec.num_requests == 1 and spec.dtype == "bf16"
     L = spec.seq_lens[0]
@@ -351,6 +355,133 @@ def main(argv=None):
         "oracle_check_max_abs_err": check,
     }
     print(json.dumps(line), flush=True)
+    return 0
+
+
+SWEEP_CTX = (16384, 65536, 262144)
+SWEEP_BUDGETS = ((1, 50), (1, 20), (1, 10), (1, 5))
+
+
+def sweep(args):
+    """Per layer-step time of the sparse path (score/select with the tail
+    refresh + sparse decode) for contexts 16K / 64K / 256K, budgets
+    2 / 5 / 10 / 20 % and both scoring modes at 10 %, next to the dense decode
+    and the rectification of a 32-token window.  Every figure is a HIP-graph
+    replay over several layer caches (at least 1 GiB in all, so nothing is
+    served from the 256 MB last-level cache), divided by the layer count;
+    the two calls of the step are also timed alone.  Printed as a markdown
+    table."""
+    import torch
+
+    import block_sparse_attention_resa_amd as resa
+    from synth import WORKLOADS, make_layer, make_paged
+
+    base = WORKLOADS["qwen7b_ctx256k_l28"]
+    H, g, d = base.num_kv_heads, base.group_size, base.head_dim
+    rows = []
+
+    def graph_of(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        torch.cuda.synchronize()
+        return gr
+
+    def replay_us(gr, n_items, steps=20):
+        gr.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            gr.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / steps / n_items
+
+    for L in SWEEP_CTX:
+        layer_bytes = 2 * H * L * d * 2
+        nl = max(2, min(16, -(-(1 << 30) // layer_bytes)))  # >= 1 GiB of caches: no reuse from the 256 MB cache
+        spec = base.with_(seq_lens=(L,), layers=nl, name=f"ctx{L}")
+        caches = []
+        for l in range(nl):
+            inp = make_layer(spec, seed=SEED, layer=l, device="cuda")
+            pg = make_paged(inp)
+            kv = resa.PagedKV(pg.k_pool, pg.v_pool, pg.desc_pool, pg.block_table, pg.seq_lens)
+            caches.append({"kv": kv, "q": inp.q})
+            del inp
+        cfg0 = resa.Config(num_kv_heads=H, group_size=g, head_dim=d, dtype=resa.RESA_BF16)
+        for c in caches:
+            resa.build_descriptors(cfg0, c["kv"])
+        mb = caches[0]["kv"].max_blocks
+        torch.cuda.synchronize()
+        log(f"sweep: ctx {L}, {nl} layer caches")
+
+        den = [torch.empty((1, H * g, d), device="cuda") for _ in caches]
+        ws_den = resa.alloc_workspace(cfg0, resa.OP_DENSE_DECODE, 1, mb)
+        gd = graph_of(lambda: [resa.dense_decode(cfg0, c["kv"], c["q"], o, ws_den) for c, o in zip(caches, den)])
+        us_dense = replay_us(gd, nl)
+        del gd
+
+        f = 32
+        qc = torch.randn((1, f, H * g, d), device="cuda").to(torch.bfloat16)
+        kn = torch.randn((1, f, H, d), device="cuda").to(torch.bfloat16)
+        vn = torch.randn((1, f, H, d), device="cuda").to(torch.bfloat16)
+        rout = torch.empty((1, f, H * g, d), device="cuda")
+        ws_r = resa.alloc_workspace(cfg0, resa.OP_DENSE_RECTIFY, 1, mb, chunk=f)
+        gr = graph_of(lambda: [resa.dense_rectify(cfg0, c["kv"], qc, kn, vn, rout, ws_r) for c in caches])
+        us_rect = replay_us(gr, nl, steps=5)  # rewrites the same window each time
+        del gr
+
+        variants = [(num, den_, resa.RESA_SCORE_SUM_HEADS) for num, den_ in SWEEP_BUDGETS]
+        variants.append((1, 10, resa.RESA_SCORE_MEAN_POOL))
+        for num, den_, mode in variants:
+            cfg = resa.Config(num_kv_heads=H, group_size=g, head_dim=d, dtype=resa.RESA_BF16, budget_num=num,
+                              budget_den=den_, score_mode=mode)
+            ms = resa.selection_count(cfg, mb)
+            n_sel = resa.selection_count(cfg, (L + 15) // 16)
+            st = [{"sel": torch.empty((1, H, ms), dtype=torch.int32, device="cuda"),
+                   "cnt": torch.empty((1, H), dtype=torch.int32, device="cuda"),
+                   "out": torch.empty((1, H * g, d), device="cuda"), **c} for c in caches]
+            ws_s = resa.alloc_workspace(cfg, resa.OP_SCORE_SELECT, 1, mb, ms)
+            ws_d = resa.alloc_workspace(cfg, resa.OP_SPARSE_DECODE, 1, mb, ms)
+
+            def sel(c):
+                resa.score_select(cfg, c["kv"], c["q"], c["sel"], c["cnt"], ws_s, refresh_tail=True)
+
+            def dec(c):
+                resa.sparse_decode(cfg, c["kv"], c["q"], c["sel"], c["cnt"], c["out"], ws_d)
+
+            gs = graph_of(lambda: [(sel(c), dec(c)) for c in st])
+            us_step = replay_us(gs, nl)
+            del gs
+            gsel = graph_of(lambda: [sel(c) for c in st])
+            t_sel = replay_us(gsel, nl)
+            gdec = graph_of(lambda: [dec(c) for c in st])
+            t_dec = replay_us(gdec, nl)
+            del gsel, gdec
+            desc_b = H * ((L + 15) // 16) * 2 * d * 2
+            kv_b = H * ((n_sel - 1) * 16 + (L - ((L + 15) // 16 - 1) * 16)) * 2 * d * 2
+            rows.append({"ctx": L, "budget": f"{num}/{den_}", "mode": "sum" if mode == 0 else "mean-pool",
+                         "n_sel": n_sel, "us_step": us_step, "us_score_select": t_sel, "us_decode": t_dec,
+                         "us_dense": us_dense, "us_rectify_f32": us_rect,
+                         "gbps": (desc_b + kv_b) / (us_step * 1e-6) / 1e9,
+                         "speedup": us_dense / us_step,
+                         "cycle_speedup": us_dense / (us_step + us_rect / f)})
+            del st
+        del caches, den
+        torch.cuda.empty_cache()
+
+    print("| ctx | budget | scoring | blocks | us/layer-step | score+select us | sparse decode us | GB/s (alg.) "
+          "| dense us | x dense | rectify f=32 us | x dense incl. rectify/32 |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['ctx']} | {r['budget']} | {r['mode']} | {r['n_sel']} | {r['us_step']:.1f} | "
+              f"{r['us_score_select']:.1f} | {r['us_decode']:.1f} | {r['gbps']:.0f} | {r['us_dense']:.1f} | "
+              f"{r['speedup']:.2f} | {r['us_rectify_f32']:.0f} | {r['cycle_speedup']:.2f} |")
     return 0
 
 
