@@ -204,23 +204,6 @@ def main(argv=None):
         wall = (time.perf_counter() - w0) * 1e3 / steps
         return wall, e0.elapsed_time(e1) / steps
 
-    def time_calls(fn, reps=1):
-        """Average GPU duration of one call (HIP events bracketing the call on
-        torch's stream; a preceding GPU sleep keeps the launches queued, so the
-        interval holds the call's kernels only)."""
-        pairs = []
-        for _ in range(reps):
-            for st in layers:
-                torch.cuda._sleep(200_000)
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record()
-                fn(st)
-                b.record()
-                pairs.append((a, b))
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3  # us
-
     # ---------------------------------------------------------------- sparse step
     g_sparse = capture(sparse_step)
     log("captured sparse step graph")
@@ -228,10 +211,18 @@ def main(argv=None):
     us_layer = wall_ms * 1e3 / nlayers
     log(f"sparse: {wall_ms:.3f} ms/step (events {ev_ms:.3f}), {us_layer:.2f} us/layer-step")
 
-    # per-call breakdown (eager, queued behind a GPU sleep)
-    t_tail = time_calls(tail_refresh)
-    t_sel = time_calls(score_select)
-    t_dec = time_calls(sparse_decode)
+    # Per-call breakdown: each call alone, replayed from a graph over the 28
+    # layers and timed with HIP events on the replay stream; the sparse decode
+    # figure is the roofline kernel's average launch duration.
+    def per_call(fn):
+        gr = capture(lambda: [fn(st) for st in layers])
+        _, ev = time_graph(gr, max(5, args.steps // 5), 2)
+        del gr
+        return ev * 1e3 / nlayers  # us
+
+    t_tail = per_call(tail_refresh)
+    t_sel = per_call(score_select)
+    t_dec = per_call(sparse_decode)
     log(f"breakdown us: tail-descriptor call {t_tail:.2f}  score+select (with tail refresh) {t_sel:.2f}  "
         f"sparse decode {t_dec:.2f}")
 
@@ -307,7 +298,7 @@ def main(argv=None):
     def rectify(st):
         resa.dense_rectify(cfg, st["kv"], qc, kn, vn, rout, ws_rect)
 
-    t_rect = time_calls(rectify)
+    t_rect = per_call(rectify)  # every replay rewrites the same window
     rect_flops = H * g * sum(4 * d * (L - RECT_CHUNK + t + 1) for t in range(RECT_CHUNK))
     log(f"rectify (window {RECT_CHUNK}): {t_rect:.1f} us/layer, {rect_flops / (t_rect * 1e-6) / 1e12:.1f} TFLOP/s")
 
