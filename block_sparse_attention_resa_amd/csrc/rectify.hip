@@ -200,21 +200,22 @@ __global__ __launch_bounds__(kRectThreads) void rectify_attn_kernel(
 // bf16 chunk attention with K / V streamed through LDS.  A 512-thread
 // workgroup owns up to 256 query rows of one KV head (8 wavefronts x two
 // 16-column tiles) and walks one split of the cache two blocks (32 tokens)
-// per step.  The blocks of the next kRlStages - 1 steps are in flight as
-// direct global-to-LDS copies (no registers held), into a ring of LDS
-// stages, so each K / V byte leaves HBM once per workgroup and is read from
-// LDS by all eight wavefronts.  Both products use v_mfma_f32_16x16x32_bf16:
-// S^T = K . Q^T per block, and O^T += V^T . P^T over the two blocks at once,
-// the contraction slots of a lane holding tokens 4q..4q+3 of each block in
-// both operands.  P enters as a bf16 high part and a bf16 residual, as in
-// decode.  Key rows are stored with their 16-byte pieces XOR-swizzled by row
-// so the sixteen rows a wavefront reads together fall in different banks.
+// per step.  The blocks of the next steps are in flight as direct
+// global-to-LDS copies (no registers held) into a ring of LDS stages, so each
+// K / V byte leaves HBM once per workgroup and is read from LDS by all eight
+// wavefronts.  Both products use v_mfma_f32_16x16x32_bf16: S^T = K . Q^T as
+// two 16-token score tiles per step, and O^T += V^T . P^T over the step's 32
+// tokens at once, the contraction slots of a lane holding eight consecutive
+// tokens in both operands.  P enters as a bf16 high part and a bf16
+// residual, as in decode.  Key and value pieces are XOR-swizzled in LDS so
+// that the rows (channels) a wavefront reads together fall in different
+// banks.
 constexpr int kRlWaves = 8;
 constexpr int kRlThreads = 64 * kRlWaves;
 constexpr int kRlTiles = 2;                         // 16-column tiles per wavefront
 constexpr int kRlRows = kRlWaves * kRlTiles * 16;  // query rows per workgroup
 constexpr int kRlStep = 2;                          // blocks per step
-constexpr int kRlStages = 6;                        // LDS ring: steps in flight + the one computed
+constexpr int kRlStages = 8;                        // LDS ring stages (one step each)
 constexpr int kRlPidMax = 2048;                     // blocks per split (physical ids kept in LDS)
 
 template <int D>
@@ -227,8 +228,23 @@ struct RectLds {
   static constexpr int ISSUES = 2 * KPIECES / kRlThreads;  // copies per wavefront per step
   static_assert(2 * KPIECES % kRlThreads == 0, "a step is a whole number of copies per wavefront");
   static_assert(KPIECES % 64 == 0, "a wavefront copies keys or values, not both");
-  // piece index of (row, logical piece c) inside a key block
-  __device__ static int kpiece(int row, int c) { return row * CPR + (c ^ ((row / (16 / CPR)) % CPR)); }
+  static_assert(CPR == 8 || CPR == 16, "head dims 64 and 128");
+  // The two score tiles of a step take tokens {8a + e} and {8a + 4 + e}
+  // (a < 4, e < 4), so that a lane's eight probabilities cover eight
+  // consecutive tokens, which lie in one 16-byte value piece.  Key rows are
+  // XOR-swizzled so that the sixteen rows of either tile fall in distinct
+  // 16-byte bank groups: with 256-byte rows (d = 128) a row's swizzle takes
+  // bits 0-1 and 3-4 of the token, with 128-byte rows (two to a bank row)
+  // bits 1 and 3-4.
+  __device__ static int kswz(int token) {
+    return CPR == 16 ? (token & 3) | ((token >> 1) & 12) : ((token >> 1) & 1) | ((token >> 2) & 6);
+  }
+  // piece index of (token, logical piece c) inside the keys of a step
+  __device__ static int kpiece(int token, int c) { return token * CPR + (c ^ kswz(token)); }
+  // piece index of (channel, token half h) inside a value block: the halves
+  // swap for channels with bit 3 set, so the sixteen channels a wavefront
+  // reads together fall in distinct bank groups
+  __device__ static int vpiece(int ch, int h) { return ch * 2 + (h ^ ((ch >> 3) & 1)); }
 };
 
 // One 16-byte piece per lane from global memory straight into LDS at
@@ -237,10 +253,16 @@ struct RectLds {
 // otherwise wait for every copy in flight before any LDS read from a stage
 // it cannot tell apart.  The instruction writes no register; its completion
 // is awaited explicitly (vmcnt in ring_sync) before the stage is read.
-__device__ __forceinline__ void copy_to_lds16(const bf16_t* src, bf16_t* lds_wave) {
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)lds_wave);  // LDS byte offset
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src)
+// The source is a wavefront-uniform base (scalar registers) plus a 32-bit
+// byte offset per lane; the destination is an LDS byte address.
+__device__ __forceinline__ void copy_to_lds16(const bf16_t* base_ptr, uint32_t voff, uint32_t lds_dst) {
+  const uint64_t b = (uint64_t)(uintptr_t)base_ptr;  // uniform; read from the first lane into scalar registers
+  // (the builtin returns int: both halves are taken as uint32_t, so the low
+  // half is zero-extended)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_dst), "v"(voff), "s"(base)
                : "memory", "m0");
 }
 
@@ -275,7 +297,7 @@ __global__ __launch_bounds__(kRlThreads) void rectify_attn_lds_kernel(
   const int i = blockIdx.z % H;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address math
   const int col = lane & 15;
   const int quad = lane >> 4;
 
@@ -338,30 +360,47 @@ __global__ __launch_bounds__(kRlThreads) void rectify_attn_lds_kernel(
   __syncthreads();
 
   // Copies of one step into one stage: every wavefront moves ISSUES x 64
-  // pieces of 16 bytes straight from HBM into LDS.  Blocks past `end` copy an
-  // in-range block (the first of the split) and are masked when computed.
+  // pieces of 16 bytes straight from HBM into LDS.  Which pieces a lane
+  // moves is the same for every step: copy u of a wavefront takes keys or
+  // values (uniform) of block cb[u] of the step (uniform), at byte offset
+  // cvoff[u] of that block's tile.  Blocks past `end` copy an in-range block
+  // (the first of the split) and are masked when computed.
   const size_t head_stride = (size_t)kBlock * D;
-  auto issue = [&](int step, int stage) {
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)lds);  // LDS byte address
+  bool ck[LY::ISSUES];
+  int cb[LY::ISSUES];
+  uint32_t cvoff[LY::ISSUES];
+#pragma unroll
+  for (int u = 0; u < LY::ISSUES; ++u) {
+    const int p0 = u * kRlThreads + wave * 64;  // first piece of this copy (wavefront-uniform)
+    ck[u] = p0 < LY::KPIECES;
+    const int pp = (ck[u] ? p0 : p0 - LY::KPIECES) + lane;
+    cb[u] = (ck[u] ? p0 : p0 - LY::KPIECES) / LY::PIECES;
+    const int w = pp % LY::PIECES;
+    if (ck[u]) {
+      const int token = pp / LY::CPR;  // token of the step
+      const int c = (pp % LY::CPR) ^ LY::kswz(token);  // logical piece stored here
+      cvoff[u] = (uint32_t)(((token % kBlock) * D + c * 8) * sizeof(bf16_t));
+    } else {
+      const int ch = w / 2;
+      const int h = (w % 2) ^ ((ch >> 3) & 1);  // token half stored here
+      cvoff[u] = (uint32_t)((ch * kBlock + h * 8) * sizeof(bf16_t));
+    }
+  }
+  // The physical ids a step's copies need are read from LDS one pair of
+  // steps ahead, so the copies themselves wait for nothing.
+  auto read_pids = [&](int step, int (&pid)[LY::ISSUES]) {
+#pragma unroll
+    for (int u = 0; u < LY::ISSUES; ++u) pid[u] = s_pid[max(min(step * kRlStep + cb[u], nblk - 1), 0)];
+  };
+  auto issue = [&](int stage, const int (&pids)[LY::ISSUES]) {
 #pragma unroll
     for (int u = 0; u < LY::ISSUES; ++u) {
-      const int p0 = u * kRlThreads + wave * 64;  // first piece of this copy (wavefront-uniform)
-      const int piece = p0 + lane;
-      const bool is_k = p0 < LY::KPIECES;
-      const int pp = is_k ? piece : piece - LY::KPIECES;
-      const int b = pp / LY::PIECES;
-      const int w = pp % LY::PIECES;
-      const int gb = min(step * kRlStep + b, nblk - 1);
-      const int pid = clampi(s_pid[max(gb, 0)], 0, num_pool_blocks - 1);
-      const size_t tile = ((size_t)pid * H + i) * head_stride;
-      const bf16_t* src;
-      if (is_k) {
-        const int row = w / LY::CPR;
-        const int c = (w % LY::CPR) ^ ((row / (16 / LY::CPR)) % LY::CPR);  // logical piece stored here
-        src = k_pool + tile + (size_t)row * D + c * 8;
-      } else {
-        src = v_pool + tile + (size_t)w * 8;
-      }
-      copy_to_lds16(src, lds + stage * LY::STAGE + p0 * 8);
+      const int pid = __builtin_amdgcn_readfirstlane(clampi(pids[u], 0, num_pool_blocks - 1));
+      const bf16_t* base = (ck[u] ? k_pool : v_pool) + ((size_t)pid * H + i) * head_stride;
+      copy_to_lds16(base, cvoff[u],
+                    lds_base + (uint32_t)((stage * LY::STAGE + (u * kRlThreads + wave * 64) * 8) * sizeof(bf16_t)));
     }
   };
 
@@ -370,145 +409,236 @@ __global__ __launch_bounds__(kRlThreads) void rectify_attn_lds_kernel(
   const int first_row = rg * kRlRows + wave * kRlTiles * 16;
   const int lim_lo = first_row < rows && P0 >= 0 ? P0 + first_row / G : -1;
 
-  // One step: scores, online softmax, output update (the hardware exp2, whose
-  // results below 2^-126 flush to zero, which changes no sum beyond fp32
-  // rounding).  The reference maximum
-  // m_ref is raised only when a column's new maximum exceeds it by more than
-  // 8 (log2 units), so most steps skip rescaling the accumulators; the
-  // probabilities then stay below 2^8, and the merge, which weighs each
-  // split by 2^(m - max m), is exact for any reference value.
-  auto compute = [&](const bf16_t* kb, const bf16_t* vb, int blk0, auto masked) {
-    floatx4_t sv[kRlStep][kRlTiles];
+  // The steps are software-pipelined inside each wavefront so that the
+  // matrix unit and the vector ALU work at the same time: the scores of step
+  // s + 1 (MFMA) are computed beside the exponentials of step s (vector
+  // ALU), and the output update of step s (MFMA) beside the conversion of
+  // its probabilities to bf16 operands (vector ALU).  The hardware exp2
+  // flushes results below 2^-126 to zero, which changes no sum beyond fp32
+  // rounding.  Probabilities are taken against a per-column reference m_ref
+  // that is raised only when some probability would exceed 2^8, i.e. when a
+  // column maximum passes the reference by more than 8 (log2 units); most
+  // steps therefore need neither column maxima nor a rescale of the
+  // accumulators, and the merge, which weighs each split by 2^(m - max m),
+  // is exact for any reference value.
+  // Key operands of score tile u: row r holds token 8 (r / 4) + 4 u + r % 4.
+  // The swizzle of token t + 4 equals that of t (bit 2 of t is clear), so
+  // tile 1 lies 4 rows past tile 0.
+  int k_off[KK];
 #pragma unroll
-    for (int b = 0; b < kRlStep; ++b) {
-      uint4 kf[KK];
+  for (int kk = 0; kk < KK; ++kk) k_off[kk] = LY::kpiece(8 * (col >> 2) + (col & 3), quad * KK + kk) * 8;
+  auto load_k = [&](const bf16_t* kb, uint4 (&kf)[kRlStep][KK]) {
+#pragma unroll
+    for (int u = 0; u < kRlStep; ++u)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        kf[kk] = *reinterpret_cast<const uint4*>(kb + b * LY::BLK + LY::kpiece(col, quad * KK + kk) * 8);
+        kf[u][kk] = *reinterpret_cast<const uint4*>(kb + k_off[kk] + u * 4 * LY::CPR * 8);
+  };
+  auto qk = [&](const uint4 (&kf)[kRlStep][KK], floatx4_t (&sv)[kRlStep][kRlTiles]) {
+#pragma unroll
+    for (int b = 0; b < kRlStep; ++b)
 #pragma unroll
       for (int c = 0; c < kRlTiles; ++c) {
         floatx4_t x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-          x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]),
+          x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[b][kk]),
                                                       __builtin_bit_cast(bf16x8_t, qf[c][kk]), x, 0, 0, 0);
         sv[b][c] = x;
       }
-    }
-    // Value operands of both blocks, shared by every tile: V^T slots 0-3 are
-    // block 0 tokens 4q..4q+3, slots 4-7 block 1.  Entries of blocks past the
-    // split and of tokens past the sequence end are zeroed: their
-    // probability is 0 but the bytes there may be anything.
-    bf16x8_t vop[NT];
-    {
-      uint2 keep[kRlStep];
+  };
+  // Value operand of output tile t, shared by every query tile: slot j of a
+  // lane in quad q is token 8 q + j of the step (block q / 2), the same
+  // order as the probabilities.  On masked steps the entries of blocks past
+  // the split and of tokens past the sequence end are zeroed (`keep`): their
+  // probability is 0 but the bytes there may be anything.
+  // (channel 16 t + c has the swizzle of channel c, so tile t lies 16
+  // channels past tile 0)
+  const int v_off = (quad >> 1) * LY::BLK + LY::vpiece(col, quad & 1) * 8;
+  auto v_operand = [&](const bf16_t* vb, int t) {
+    return *reinterpret_cast<const uint4*>(vb + v_off + t * 16 * kBlock);
+  };
+  auto v_keep = [&](int blk0) {
+    const int vl = blk0 + (quad >> 1) < end ? L - blk0 * kBlock - 8 * quad : 0;  // valid tokens from 8q on
+    uint4 k;
+    k.x = (vl > 0 ? 0xffffu : 0u) | (vl > 1 ? 0xffff0000u : 0u);
+    k.y = (vl > 2 ? 0xffffu : 0u) | (vl > 3 ? 0xffff0000u : 0u);
+    k.z = (vl > 4 ? 0xffffu : 0u) | (vl > 5 ? 0xffff0000u : 0u);
+    k.w = (vl > 6 ? 0xffffu : 0u) | (vl > 7 ? 0xffff0000u : 0u);
+    return k;
+  };
+  // Scores past the row's last visible position (which also covers the
+  // sequence end) or past the split are excluded.  Entry e of score tile u
+  // in quad q is token 8 q + 4 u + e of the step.
+  auto mask_s = [&](int blk0, floatx4_t (&sv)[kRlStep][kRlTiles]) {
+    const bool in_split = blk0 + (quad >> 1) < end;
 #pragma unroll
-      for (int b = 0; b < kRlStep; ++b) {
-        if constexpr (decltype(masked)::value) {
-          const int vl = blk0 + b < end ? L - (blk0 + b) * kBlock - 4 * quad : 0;  // valid tokens from 4q on
-          keep[b].x = (vl > 0 ? 0xffffu : 0u) | (vl > 1 ? 0xffff0000u : 0u);
-          keep[b].y = (vl > 2 ? 0xffffu : 0u) | (vl > 3 ? 0xffff0000u : 0u);
-        } else {
-          keep[b] = make_uint2(0xffffffffu, 0xffffffffu);
-        }
-      }
+    for (int u = 0; u < kRlStep; ++u) {
+      const int tok0 = blk0 * kBlock + 8 * quad + 4 * u;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        uint2 v0 = *reinterpret_cast<const uint2*>(vb + (16 * t + col) * kBlock + 4 * quad);
-        uint2 v1 = *reinterpret_cast<const uint2*>(vb + LY::BLK + (16 * t + col) * kBlock + 4 * quad);
-        if constexpr (decltype(masked)::value) {
-          v0 = make_uint2(v0.x & keep[0].x, v0.y & keep[0].y);
-          v1 = make_uint2(v1.x & keep[1].x, v1.y & keep[1].y);
-        }
-        vop[t] = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
-      }
+      for (int c = 0; c < kRlTiles; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[u][c][e] = in_split && tok0 + e <= lim[c] ? sv[u][c][e] : -INFINITY;
     }
+  };
+  // Probabilities of a step against the references.
+  auto exps = [&](const floatx4_t (&sv)[kRlStep][kRlTiles], float (&p)[kRlTiles][kRlStep * 4]) {
+#pragma unroll
+    for (int c = 0; c < kRlTiles; ++c) {
+      const float neg_m = m_ref[c] == -INFINITY ? 0.f : -m_ref[c];
+#pragma unroll
+      for (int u = 0; u < kRlStep; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[c][4 * u + e] = __builtin_amdgcn_exp2f(fmaf(sv[u][c][e], scale_log2, neg_m));
+    }
+  };
+  // True in a lane where a score of the step passes its column's reference
+  // by more than 8 (log2 units).
+  auto passes = [&](const floatx4_t (&sv)[kRlStep][kRlTiles]) {
+    bool any = false;
 #pragma unroll
     for (int c = 0; c < kRlTiles; ++c) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < kRlStep; ++b) {
-        const int tok0 = (blk0 + b) * kBlock + 4 * quad;
-        const bool in_split = blk0 + b < end;
+      for (int u = 0; u < kRlStep; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // masked: past the row's last visible position (which also covers
-          // the sequence end) or past the split
-          if constexpr (decltype(masked)::value)
-            sv[b][c][e] = in_split && tok0 + e <= lim[c] ? sv[b][c][e] : -INFINITY;
-          mx = fmaxf(mx, sv[b][c][e]);
-        }
-      }
-      mx = quad_max(mx);
-      const float m_cand = mx * scale_log2;  // scale > 0: the maximum of the scaled scores
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sv[u][c][e]);
+      any = any || mx * scale_log2 > m_ref[c] + 8.f;
+    }
+    return any;
+  };
+  // Raise the reference of every column whose maximum passes it by more than
+  // 8 to that maximum and rescale the column's accumulated output and sum.
+  auto raise_ref = [&](const floatx4_t (&sv)[kRlStep][kRlTiles]) {
+#pragma unroll
+    for (int c = 0; c < kRlTiles; ++c) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kRlStep; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sv[u][c][e]);
+      const float m_cand = quad_max(mx) * scale_log2;  // scale > 0: the maximum of the scaled scores
       const bool raise = m_cand > m_ref[c] + 8.f;
-      if (__ballot(raise)) {
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_ref[c] - m_cand) : 1.f;  // 0 while m_ref = -inf
-        m_ref[c] = raise ? m_cand : m_ref[c];
-        l_run[c] *= alpha;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_ref[c] - m_cand) : 1.f;  // 0 while m_ref = -inf
+      m_ref[c] = raise ? m_cand : m_ref[c];
+      l_run[c] *= alpha;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[c][t] *= alpha;
-      }
-      const float neg_m = m_ref[c] == -INFINITY ? 0.f : -m_ref[c];
-      float p[kRlStep * 4];
-#pragma unroll
-      for (int b = 0; b < kRlStep; ++b)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[4 * b + e] = __builtin_amdgcn_exp2f(fmaf(sv[b][c][e], scale_log2, neg_m));
-          l_run[c] += p[4 * b + e];
-        }
-      // P^T operands, same slot order as V^T: a bf16 high part and the bf16
-      // of the residual
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const bf16x2_t hi = __builtin_convertvector(float2_t{p[2 * h], p[2 * h + 1]}, bf16x2_t);
-        const float2_t hf = __builtin_convertvector(hi, float2_t);
-        const bf16x2_t lo = __builtin_convertvector(float2_t{p[2 * h] - hf.x, p[2 * h + 1] - hf.y}, bf16x2_t);
-        hw[h] = __builtin_bit_cast(uint32_t, hi);
-        lw[h] = __builtin_bit_cast(uint32_t, lo);
-      }
-      const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-      const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-      // O^T += V^T . P^T over both blocks
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[t], ph, acc[c][t], 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[t], pl, acc[c][t], 0, 0, 0);
+      for (int t = 0; t < NT; ++t) acc[c][t] *= alpha;
     }
   };
+  // Probabilities of one tile as P^T operands in the V^T slot order: a bf16
+  // high part and the bf16 of the residual.
+  auto split = [&](const float (&p)[kRlStep * 4], bf16x8_t& ph, bf16x8_t& pl) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const bf16x2_t hi = __builtin_convertvector(float2_t{p[2 * h], p[2 * h + 1]}, bf16x2_t);
+      const float2_t hf = __builtin_convertvector(hi, float2_t);
+      const bf16x2_t lo = __builtin_convertvector(float2_t{p[2 * h] - hf.x, p[2 * h + 1] - hf.y}, bf16x2_t);
+      hw[h] = __builtin_bit_cast(uint32_t, hi);
+      lw[h] = __builtin_bit_cast(uint32_t, lo);
+    }
+    ph = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    pl = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+  };
+  // O^T += V^T . P^T over both blocks of a step.
+  auto pv = [&](const bf16_t* vb, const bf16x8_t (&ph)[kRlTiles], const bf16x8_t (&pl)[kRlTiles], auto masked,
+                int blk0) {
+    uint4 keep = make_uint4(~0u, ~0u, ~0u, ~0u);
+    if constexpr (decltype(masked)::value) keep = v_keep(blk0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint4 v = v_operand(vb, t);
+      if constexpr (decltype(masked)::value) v = make_uint4(v.x & keep.x, v.y & keep.y, v.z & keep.z, v.w & keep.w);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, v);
+#pragma unroll
+      for (int c = 0; c < kRlTiles; ++c) {
+        acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[c], acc[c][t], 0, 0, 0);
+        acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[c], acc[c][t], 0, 0, 0);
+      }
+    }
+  };
+  // Steps wholly inside the split, the sequence and every row's causal
+  // window (all but the last few) skip the masking.
+  auto plain = [&](int s) {
+    const int blk0 = beg + s * kRlStep;
+    return blk0 + kRlStep <= end && (blk0 + kRlStep) * kBlock - 1 <= lim_lo;
+  };
 
-  // Steps go in pairs, one barrier per pair: pair (s, s + 1) is computed
-  // from stages s % NS and (s + 1) % NS while the copies of the next
-  // NS - 2 steps are in flight; after the barrier the two stages of the
-  // previous pair are free and receive steps s + NS - 2 and s + NS - 1.
-  static_assert(NS % 2 == 0 && NS >= 4, "stages come in pairs");
+  floatx4_t scur[kRlStep][kRlTiles];  // scores of the step about to be computed
+  // Step s: scores of step s + 1 (for the last step, scores of a stage
+  // already read, unused), then probabilities and output update of step s.
+  // `masked` steps apply the split, sequence and causal masks.
+  auto body = [&](int s, auto masked) {
+    const bool has_next = s + 1 < nsteps;
+    const bf16_t* kb_next = lds + ((has_next ? s + 1 : s) % NS) * LY::STAGE;
+    const bf16_t* vb = lds + (s % NS) * LY::STAGE + kRlStep * LY::BLK;
+    const int blk0 = beg + s * kRlStep;
+    uint4 kf[kRlStep][KK];
+    load_k(kb_next, kf);
+    floatx4_t snext[kRlStep][kRlTiles];
+    qk(kf, snext);
+    float p[kRlTiles][kRlStep * 4];
+    exps(scur, p);
+    if constexpr (decltype(masked)::value) mask_s(blk0 + kRlStep, snext);
+    bf16x8_t ph[kRlTiles], pl[kRlTiles];
+#pragma unroll
+    for (int c = 0; c < kRlTiles; ++c) {
+#pragma unroll
+      for (int j = 0; j < kRlStep * 4; ++j) l_run[c] += p[c][j];
+      split(p[c], ph[c], pl[c]);
+    }
+    pv(vb, ph, pl, masked, blk0);
+    // rare: a column maximum of step s + 1 passes its reference by more than 8
+    if (__ballot(has_next && passes(snext))) raise_ref(snext);
+#pragma unroll
+    for (int u = 0; u < kRlStep; ++u)
+#pragma unroll
+      for (int c = 0; c < kRlTiles; ++c) scur[u][c] = snext[u][c];
+  };
+
+  // Ring protocol, one barrier per pair of steps.  Step s lives in stage
+  // s % NS.  Step s reads the values of step s and the keys of step s + 1,
+  // so the barrier before pair (s, s + 1) waits until the copies of steps
+  // <= s + 2 have landed (those of up to NS - 5 later steps may still be in
+  // flight) and then refills the stages of steps s - 2 and s - 1, which no
+  // wavefront reads any more, with steps s + NS - 2 and s + NS - 1.
+  static_assert(NS % 2 == 0 && NS >= 6 && NS - 5 <= 3, "stages come in pairs; at most three steps pending");
 #pragma unroll
   for (int j = 0; j < NS - 2; ++j)
-    if (j < nsteps) issue(j, j);
-  int stage = 0;
+    if (j < nsteps) {
+      int pj[LY::ISSUES];
+      read_pids(j, pj);
+      issue(j, pj);
+    }
+  int pf0[LY::ISSUES], pf1[LY::ISSUES];  // ids for the next pair's copies
+  read_pids(NS - 2, pf0);
+  read_pids(NS - 1, pf1);
 #pragma clang loop unroll(disable)
   for (int step = 0; step < nsteps; step += 2) {
-    // this pair's copies are done once at most the next pair's are pending
-    if (step + NS - 3 < nsteps) ring_sync<LY::ISSUES * 2>();
+    const int pending = min(min(step + NS - 3, nsteps - 1) - (step + 2), NS - 5);
+    if (pending >= 3) ring_sync<3 * LY::ISSUES>();
+    else if (pending == 2) ring_sync<2 * LY::ISSUES>();
+    else if (pending == 1) ring_sync<LY::ISSUES>();
     else ring_sync<0>();
-    const int freed = stage == 0 ? NS - 2 : stage - 2;  // stages of the previous pair
-    if (step + NS - 2 < nsteps) issue(step + NS - 2, freed);
-    if (step + NS - 1 < nsteps) issue(step + NS - 1, freed + 1);
+    if (step + NS - 2 < nsteps) issue((step + NS - 2) % NS, pf0);
+    if (step + NS - 1 < nsteps) issue((step + NS - 1) % NS, pf1);
+    read_pids(step + NS, pf0);
+    read_pids(step + NS + 1, pf1);
+    if (step == 0) {
+      uint4 kf[kRlStep][KK];
+      load_k(lds, kf);
+      qk(kf, scur);
+      if (!plain(0)) mask_s(beg, scur);
+      if (__ballot(passes(scur))) raise_ref(scur);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const bf16_t* kb = lds + (stage + h) * LY::STAGE;
-      const bf16_t* vb = kb + kRlStep * LY::BLK;
-      const int blk0 = beg + (step + h) * kRlStep;
-      // Steps wholly inside the split, the sequence and every row's causal
-      // window (all but the last few) skip the masking.
-      const bool plain = blk0 + kRlStep <= end && (blk0 + kRlStep) * kBlock - 1 <= lim_lo;
-      if (plain) compute(kb, vb, blk0, std::integral_constant<bool, false>{});
-      else compute(kb, vb, blk0, std::integral_constant<bool, true>{});
-      __builtin_amdgcn_sched_barrier(0);  // keep the two steps' live ranges apart
+      const int s = step + h;
+      if (h == 1 && s >= nsteps) break;
+      if (plain(s) && (s + 1 >= nsteps || plain(s + 1))) body(s, std::integral_constant<bool, false>{});
+      else body(s, std::integral_constant<bool, true>{});
     }
-    stage = stage == NS - 2 ? 0 : stage + 2;
   }
   ring_sync<0>();  // no copy may still be writing when the workgroup ends
 
