@@ -498,7 +498,8 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
   __shared__ uint32_t lds_min[NW], lds_max[NW];
   __shared__ uint32_t bucket[kFinishMax];
   __shared__ int tab[TAB];
-  __shared__ int bc[3];
+  __shared__ int bc2[2][3];  // boundary record of a pass (bin, rank left, keys), by pass parity
+  __shared__ int packed;      // keys of the boundary bucket packed so far
 
   const int i = blockIdx.x;
   const int r = blockIdx.y;
@@ -535,7 +536,11 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
 
   kr.set_count(C);
   const int R = kr.nrounds();
-  for (int b = tid; b <= kBins; b += NT) hist2[0][b] = 0u;  // published by the next barrier
+  for (int b = tid; b <= kBins; b += NT) {  // published by the next barrier
+    hist2[0][b] = 0u;
+    hist2[1][b] = 0u;
+  }
+  if (tid == 0) packed = 0;
 
   // Key range of all candidates.
   uint32_t mn = 0xffffffffu, mx = 0u;
@@ -575,7 +580,6 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     BinMap map;
     map.init(bk.lo, bk.hi, npass == 0);
     uint32_t* hist = hist2[npass & 1];
-    uint32_t* hist_next = hist2[(npass + 1) & 1];
     if (npass == 0) {  // every candidate is in the bucket
 #define RESA_COUNT_KEY(BIN)                                         \
   {                                                                 \
@@ -596,7 +600,6 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
         if (in && bk.has(x)) atomicAdd(&hist[map(x)], 1u);
       });
     }
-    for (int b = tid; b <= kBins; b += NT) hist_next[b] = 0u;  // next pass's histogram
     __syncthreads();
     // Suffix counts: thread t owns bins [BPT*rt, BPT*rt + BPT) with rt = NT-1-t,
     // so an exclusive scan in thread order counts the keys in higher bins.
@@ -610,6 +613,11 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     }
     int tot;
     const int above0 = block_exclusive_scan<NT>(c, lds_waves, tot);
+    int* bc = bc2[npass & 1];
+    // this pass's histogram is read; clear it for the pass after next
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) hist[BPT * rt + e] = 0u;
+    if (tid < (kBins + 1) - BPT * NT) hist[BPT * NT + tid] = 0u;
     if (above0 < remaining && above0 + c >= remaining) {
       int above = above0;
 #pragma unroll
@@ -627,8 +635,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     bk.bin = bc[0];
     remaining = bc[1];
     bucket_n = bc[2];
-    ++npass;
-    __syncthreads();
+    ++npass;  // the next pass writes the other record, so no barrier is needed here
   }
 
   // The threshold: the remaining-th largest key of the bucket.  Keys above it
@@ -640,12 +647,10 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     take_eq = remaining;
     n_eq = bucket_n;
   } else if (bucket_n <= kFinishMax) {
-    // Ranking finish: the bucket's keys are packed into LDS (offsets from a
-    // scan of per-thread member counts), then each member counts the members
-    // above and equal to it; the one whose rank range holds `remaining` is
-    // the threshold.
-    unsigned long long mask = 0;  // KPT > 0: member bit per round
-    int cnt = 0;
+    // Ranking finish: the bucket's keys are packed into LDS (slots handed out
+    // by an LDS counter: their order does not matter), then each member
+    // counts the members above and equal to it; the one whose rank range
+    // holds `remaining` is the threshold.
     const bool kept = kKeepBins && npass == 1;
     RESA_FOR_KEYS({
       bool m;
@@ -655,22 +660,14 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
       } else {
         m = in && bk.has(kr.key(j));
       }
-      if constexpr (KPT > 0) mask |= (m ? 1ull : 0ull) << j;
-      cnt += m ? 1 : 0;
-    });
-    int tot;
-    int pos = block_exclusive_scan<NT>(cnt, lds_waves, tot);
-    RESA_FOR_KEYS({
-      bool m;
-      if constexpr (KPT > 0) m = (mask >> j) & 1ull;
-      else m = in && bk.has(kr.key(j));
       if (m) {
+        const int pos = atomicAdd(&packed, 1);
         if (pos < kFinishMax) bucket[pos] = kr.key(j);
-        ++pos;
       }
     });
     __syncthreads();
-    const int nb = tot < kFinishMax ? tot : kFinishMax;
+    const int nb = bucket_n;  // the members counted by the last pass
+    int* bc = bc2[npass & 1];  // the record the last pass did not use
     if (tid < nb) {
       const uint32_t x = bucket[tid];
       int gt = 0, eq = 0;
