@@ -189,26 +189,32 @@ def main(argv=None):
         torch.cuda.synchronize()
         return graph
 
-    def time_graph(graph, steps, warmup):
+    def time_graph(graph, steps, warmup, per_step=None):
+        """Mean ms per replay (wall clock between synchronizations, and HIP
+        events on the stream); with `per_step` a list, it receives each
+        replay's event-timed duration."""
         for _ in range(warmup):
             graph.replay()
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         w0 = time.perf_counter()
-        e0.record()
-        for _ in range(steps):
+        ev[0].record()
+        for k in range(steps):
             graph.replay()
-        e1.record()
+            ev[k + 1].record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - w0) * 1e3 / steps
-        return wall, e0.elapsed_time(e1) / steps
+        if per_step is not None:
+            per_step.extend(ev[k].elapsed_time(ev[k + 1]) for k in range(steps))
+        return wall, ev[0].elapsed_time(ev[steps]) / steps
 
     # ---------------------------------------------------------------- sparse step
     g_sparse = capture(sparse_step)
     log("captured sparse step graph")
-    wall_ms, ev_ms = time_graph(g_sparse, args.steps, args.warmup)
+    step_ms = []
+    wall_ms, ev_ms = time_graph(g_sparse, args.steps, args.warmup, per_step=step_ms)
     us_layer = wall_ms * 1e3 / nlayers
+    pct = {f"p{q}": round(float(np.percentile(step_ms, q)) * 1e3 / nlayers, 3) for q in (10, 50, 90)}
     log(f"sparse: {wall_ms:.3f} ms/step (events {ev_ms:.3f}), {us_layer:.2f} us/layer-step")
 
     # Per-call breakdown: each call alone, replayed from a graph over the 28
@@ -328,6 +334,7 @@ def main(argv=None):
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_layer_step": ab["total"],
+        "us_per_layer_step_percentiles": pct,
         "tokens_per_s": round(1e3 / wall_ms, 1),
         "dense_us_per_layer_step": round(us_dense, 3),
         "speedup_vs_dense": round(us_dense / us_layer, 3),
