@@ -94,6 +94,9 @@ def main(argv=None):
                     help="also run one plain device copy of this size (HBM counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line: context x budget x scoring-mode table (markdown)")
+    ap.add_argument("--workloads", action="store_true",
+                    help="instead of the headline line: every bf16 workload (batch, ragged, 131K + rectify) "
+                         "as a markdown table")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -114,6 +117,8 @@ def main(argv=None):
     torch.cuda.set_device(0)
     if args.sweep:
         return sweep(args)
+    if args.workloads:
+        return workloads(args)
     spec = WORKLOADS[args.workload]
     assert spec.num_requests == 1 and spec.dtype == "bf16"
     L = spec.seq_lens[0]
@@ -480,6 +485,126 @@ def sweep(args):
         print(f"| {r['ctx']} | {r['budget']} | {r['mode']} | {r['n_sel']} | {r['us_step']:.1f} | "
               f"{r['us_score_select']:.1f} | {r['us_decode']:.1f} | {r['gbps']:.0f} | {r['us_dense']:.1f} | "
               f"{r['speedup']:.2f} | {r['us_rectify_f32']:.0f} | {r['cycle_speedup']:.2f} |")
+    return 0
+
+
+WORKLOAD_TABLE = ("qwen7b_ctx32k_b1", "qwen7b_ragged_b8", "qwen7b_ctx131k_b4_rectify", "qwen7b_ctx256k_l28")
+
+
+def workloads(args):
+    """The bf16 workloads of the measured configurations, each at its own
+    batch and context: per layer-step time of the sparse step (score/select
+    with the tail refresh + sparse decode, all requests of one layer), decode
+    tokens/s over 28 layers (attention only), algorithmic GB/s and its
+    fraction of 8 TB/s, the dense decode and the speedup, and the
+    rectification of the workload's window (the rectify workload's f, else
+    32) with its useful TFLOP/s and fraction of the 2.5 PFLOP/s bf16 MFMA
+    peak.  HIP-graph replays over several layer caches (at least 1 GiB in
+    all), divided by the layer count.  Printed as a markdown table."""
+    import torch
+
+    import block_sparse_attention_resa_amd as resa
+    from synth import WORKLOADS, make_layer, make_paged
+
+    def graph_of(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        torch.cuda.synchronize()
+        return gr
+
+    def replay_us(gr, n_items, steps):
+        gr.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            gr.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / steps / n_items
+
+    rows = []
+    for name in WORKLOAD_TABLE:
+        spec = WORKLOADS[name]
+        H, g, d, e = spec.num_kv_heads, spec.group_size, spec.head_dim, 2
+        cfg = resa.Config(num_kv_heads=H, group_size=g, head_dim=d, dtype=resa.RESA_BF16)
+        lens = None
+        caches = []
+        nl = 2
+        l = 0
+        while l < nl:
+            inp = make_layer(spec, seed=SEED, layer=l, device="cuda")
+            lens = list(inp.seq_lens)
+            if l == 0:
+                layer_bytes = sum(2 * H * L * d * e for L in lens)
+                nl = max(2, min(16, -(-(1 << 30) // layer_bytes)))
+            pg = make_paged(inp)
+            kv = resa.PagedKV(pg.k_pool, pg.v_pool, pg.desc_pool, pg.block_table, pg.seq_lens)
+            resa.build_descriptors(cfg, kv)
+            caches.append({"kv": kv, "q": inp.q})
+            del inp
+            l += 1
+        R = len(lens)
+        mb = caches[0]["kv"].max_blocks
+        ms = resa.selection_count(cfg, mb)
+        torch.cuda.synchronize()
+        log(f"workloads: {name}, {R} requests, {nl} layer caches")
+        st = [{"sel": torch.empty((R, H, ms), dtype=torch.int32, device="cuda"),
+               "cnt": torch.empty((R, H), dtype=torch.int32, device="cuda"),
+               "out": torch.empty((R, H * g, d), device="cuda"), **c} for c in caches]
+        ws_s = resa.alloc_workspace(cfg, resa.OP_SCORE_SELECT, R, mb, ms)
+        ws_d = resa.alloc_workspace(cfg, resa.OP_SPARSE_DECODE, R, mb, ms)
+        ws_n = resa.alloc_workspace(cfg, resa.OP_DENSE_DECODE, R, mb)
+
+        def step(c):
+            resa.score_select(cfg, c["kv"], c["q"], c["sel"], c["cnt"], ws_s, refresh_tail=True)
+            resa.sparse_decode(cfg, c["kv"], c["q"], c["sel"], c["cnt"], c["out"], ws_d)
+
+        gs = graph_of(lambda: [step(c) for c in st])
+        us_step = replay_us(gs, nl, 20)
+        del gs
+        gd = graph_of(lambda: [resa.dense_decode(cfg, c["kv"], c["q"], c["out"], ws_n) for c in st])
+        us_dense = replay_us(gd, nl, 10)
+        del gd
+
+        f = getattr(spec, "rectify_chunk", 0) or 32
+        qc = torch.randn((R, f, H * g, d), device="cuda").to(torch.bfloat16)
+        kn = torch.randn((R, f, H, d), device="cuda").to(torch.bfloat16)
+        vn = torch.randn((R, f, H, d), device="cuda").to(torch.bfloat16)
+        rout = torch.empty((R, f, H * g, d), device="cuda")
+        ws_r = resa.alloc_workspace(cfg, resa.OP_DENSE_RECTIFY, R, mb, chunk=f)
+        gr = graph_of(lambda: [resa.dense_rectify(cfg, c["kv"], qc, kn, vn, rout, ws_r) for c in caches])
+        us_rect = replay_us(gr, nl, 5)  # rewrites the same windows each time
+        del gr
+
+        alg = 0
+        nsel = []
+        for L in lens:
+            n = resa.selection_count(cfg, (L + 15) // 16)
+            nsel.append(n)
+            alg += algorithmic_bytes(spec, L, n, e)["total"]
+        flops = sum(H * g * 4 * d * (L - f + t + 1) for L in lens for t in range(f))
+        gbps = alg / (us_step * 1e-6) / 1e9
+        rows.append({"name": name, "R": R, "ctx": f"{min(lens)}" if min(lens) == max(lens) else f"{min(lens)}-{max(lens)}",
+                     "nsel": f"{min(nsel)}" if min(nsel) == max(nsel) else f"{min(nsel)}-{max(nsel)}",
+                     "us": us_step, "tok": R / (28 * us_step * 1e-6), "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS,
+                     "dense": us_dense, "x": us_dense / us_step, "f": f, "rect": us_rect,
+                     "tflops": flops / (us_rect * 1e-6) / 1e12})
+        del st, caches, qc, kn, vn, rout
+        torch.cuda.empty_cache()
+
+    print("| workload | requests | context | blocks/head | us/layer-step | tokens/s (28 layers) | GB/s (alg.) "
+          "| of 8 TB/s | dense us | x dense | rectify f | rectify us | rectify TFLOP/s | of 2.5 PFLOP/s |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['name']} | {r['R']} | {r['ctx']} | {r['nsel']} | {r['us']:.1f} | {r['tok']:.0f} | "
+              f"{r['gbps']:.0f} | {r['frac'] * 100:.1f} % | {r['dense']:.1f} | {r['x']:.2f} | {r['f']} | "
+              f"{r['rect']:.0f} | {r['tflops']:.0f} | {r['tflops'] / 2500 * 100:.1f} % |")
     return 0
 
 
