@@ -242,12 +242,13 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(
 
 // Log-sum-exp merge of split partials:
 //   out[c] = sum_s 2^(m_s - m) o_s[c] / sum_s 2^(m_s - m) l_s,  m = max_s m_s.
-// Four consecutive lanes share one output float4: lane part p folds splits
-// p, p + 4, p + 8, ... in increasing order with the running (m, l, o) update,
-// all loads of a batch of kMergeBatch splits issued before the first use;
-// the four partial states are then combined (parts 0+1, 2+3, then both) by
-// lane exchanges.  No barrier and no LDS, and the order of every sum is
-// fixed, so the result is deterministic.
+// kMergeParts consecutive lanes share one output float4: lane part p folds
+// splits p, p + kMergeParts, p + 2 kMergeParts, ... in increasing order with
+// the running (m, l, o) update, all loads of a batch of kMergeBatch splits
+// issued before the first use; the partial states are then combined by lane
+// exchanges (xor 1, 2, 4, 8), each pair in the same order on both lanes.  No
+// barrier and no LDS, and the order of every sum is fixed, so the result is
+// deterministic.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeParts = 16;  // lanes per output float4
 constexpr int kMergeBatch = 4;   // splits per lane per batch of loads
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
 #pragma unroll
     for (int b = 0; b < kMergeBatch; ++b) merge_into(st, mv[b], lv[b], ov[b]);
   }
-  // combine the four parts: xor 1 then xor 2 (lanes of one output are consecutive)
+  // combine the parts: xor 1, 2, 4, 8 (the lanes of one output are consecutive)
 #pragma unroll
   for (int off = 1; off < kMergeParts; off <<= 1) {
     const float m_o = __shfl_xor(st.m, off);
