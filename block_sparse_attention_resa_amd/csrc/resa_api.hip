@@ -116,7 +116,7 @@ size_t partial_bytes(const resa_config* c, int R, int S, long long rows_per_head
 size_t workspace_bytes(const resa_config* c, int op, int R, int max_blocks, int max_sel, int chunk) {
   switch (op) {
     case RESA_OP_SCORE_SELECT:
-      return align_up((size_t)R * c->num_kv_heads * max_blocks * sizeof(uint32_t));
+      return align_up((size_t)R * c->num_kv_heads * key_stride_for(max_blocks) * sizeof(uint32_t));
     case RESA_OP_SPARSE_DECODE:
     case RESA_OP_DENSE_DECODE: {
       const int S = splits_for(c, op, R, max_blocks, max_sel, chunk);
@@ -255,6 +255,7 @@ resa_status resa_score_select(const resa_config* cfg, const resa_paged_kv* kv, i
   sa.max_blocks = kv->max_blocks;
   sa.num_pool_blocks = kv->num_pool_blocks;
   sa.mode = cfg->score_mode;
+  sa.key_stride = key_stride_for(kv->max_blocks);
   hipError_t e = launch_scores(sa, s);
   if (e != hipSuccess) return RESA_ERR_LAUNCH;
   SelectArgs se{};
@@ -270,6 +271,7 @@ resa_status resa_score_select(const resa_config* cfg, const resa_paged_kv* kv, i
   se.budget_den = cfg->budget_den;
   se.min_blocks = cfg->min_blocks;
   se.local_blocks = cfg->local_blocks;
+  se.key_stride = sa.key_stride;
   return from_hip(launch_select(se, s));
 }
 

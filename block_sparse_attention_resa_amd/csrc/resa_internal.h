@@ -76,19 +76,25 @@ struct ScoreArgs {
   int32_t refresh_tail;
   const int32_t* table;
   const int32_t* seq_lens;
-  uint32_t* keys;  // [R][H][max_blocks] workspace
+  uint32_t* keys;  // [R][H][key_stride] workspace
   float* scores;   // nullable export [R][H][max_blocks]
   int32_t R, H, G, D, dtype, max_blocks, num_pool_blocks, mode;
+  int32_t key_stride;  // key_stride_for(max_blocks)
 };
 hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream);
 
+// Row stride of the score keys: a multiple of 4 entries, so every row starts
+// 16-byte aligned and the selection can read its keys with 16-byte loads.
+inline int key_stride_for(int max_blocks) { return (max_blocks + 3) & ~3; }
+
 struct SelectArgs {
-  const uint32_t* keys;
+  const uint32_t* keys;  // [R][H][key_stride]
   const int32_t* seq_lens;
   int32_t* sel_idx;
   int32_t* sel_cnt;
   int32_t R, H, max_blocks, max_sel;
   int32_t budget_num, budget_den, min_blocks, local_blocks;
+  int32_t key_stride;
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 

@@ -18,16 +18,17 @@
 // 32-bit keys for the selection kernel.
 //
 // Selection.  One 1024-thread workgroup per (request, KV head); thread t
-// owns candidate blocks t, t + 1024, ... (coalesced loads, kept in
-// registers).  The (n - n_local)-th largest key among the older blocks is
-// found by histogram passes in LDS over monotone bin maps: the first pass
-// bins the score range [min, max] into 2048 equal-width bins, later passes
-// (rarely needed) bin the key offsets inside the boundary bucket.  Once the
-// boundary bucket holds at most 256 keys they are packed into LDS and ranked
-// in parallel.  Blocks above the threshold are taken, blocks equal to it
-// lowest index first, and one scanned table of per-(round, wavefront) ballot
-// counts places every selected id in ascending order.  Wave-wide scans and
-// reductions use DPP lane shifts.
+// owns the consecutive candidate blocks [k t, k t + k) (16-byte loads, kept
+// in registers; rows longer than 32768 blocks fall back to blocks t, t +
+// 1024, ... re-read from memory).  The (n - n_local)-th largest key among
+// the older blocks is found by histogram passes in LDS over monotone bin
+// maps: the first pass bins the score range [min, max] into 2048
+// equal-width bins, later passes (rarely needed) bin the key offsets inside
+// the boundary bucket.  Once the boundary bucket holds at most 256 keys they
+// are packed into LDS and ranked in parallel.  Blocks above the threshold
+// are taken, blocks equal to it lowest index first, and one scan of the
+// per-thread counts places every selected id in ascending order.
+// Wave-wide scans and reductions use DPP lane shifts.
 #include "desc_unit.h"
 #include "resa_internal.h"
 
@@ -85,7 +86,8 @@ __global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, co
                                                     const int32_t* __restrict__ seq_lens,
                                                     uint32_t* __restrict__ keys, float* __restrict__ scores, int H,
                                                     int G, int max_blocks, int num_pool_blocks,
-                                                    const T* __restrict__ k_pool, T* desc_tail, int score_wgs) {
+                                                    const T* __restrict__ k_pool, T* desc_tail, int score_wgs,
+                                                    int key_stride) {
   using CL = ChunkLoad<T>;
   constexpr int VPL = CL::kVals;
   constexpr int CH = 2 * D / VPL;  // lanes per descriptor
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, co
   const int bpi = blockDim.x / (CH * H);  // blocks per iteration
   const int wg_blocks = bpi * kScoreUnroll;
   const int wg_b0 = blockIdx.x * wg_blocks;
-  uint32_t* key_row = keys + ((size_t)r * H + head) * max_blocks;
+  uint32_t* key_row = keys + ((size_t)r * H + head) * key_stride;
   float* score_row = scores ? scores + ((size_t)r * H + head) * max_blocks : nullptr;
 
   // Physical ids of this workgroup's blocks: one coalesced load per wavefront
@@ -250,7 +252,7 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((score_kernel<T, D, MODE, MAXG>), grid, dim3(threads), lds, stream,                     \
                      static_cast<const T*>(a.q), static_cast<const T*>(a.desc_pool), a.table, a.seq_lens, a.keys, \
                      a.scores, a.H, a.G, a.max_blocks, a.num_pool_blocks, static_cast<const T*>(a.k_pool),  \
-                     static_cast<T*>(const_cast<void*>(a.desc_pool)), wgs)
+                     static_cast<T*>(const_cast<void*>(a.desc_pool)), wgs, a.key_stride)
   if (a.G <= 8) {
     if (a.mode == 0) RESA_SCORE_LAUNCH(0, 8);
     else RESA_SCORE_LAUNCH(1, 8);
@@ -267,10 +269,6 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
 constexpr int kDigitBits = 11;  // histogram pass: 2048 bins
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kFinishMax = 256;  // boundary bucket size the ranking finish takes
-
-__device__ __forceinline__ unsigned lane_prefix(unsigned long long mask) {
-  return __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
-}
 
 // Cross-lane steps through DPP (row shifts within 16-lane rows, then the
 // row-15 / row-31 broadcasts), which stay in the vector ALU instead of the
@@ -352,55 +350,47 @@ __device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, uint32
   __syncthreads();  // lds_min / lds_max may be rewritten right after
 }
 
-// In-place exclusive prefix sum of tab[0, n), n <= 512, by one wavefront:
-// lane l owns entries [l*per, (l+1)*per).
-__device__ __forceinline__ void wave_scan_table(int* tab, int n) {
-  const int lane = threadIdx.x & 63;
-  const int per = (n + 63) / 64;
-  int v[8];
-  int sum = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int idx = lane * per + e;
-    v[e] = (e < per && idx < n) ? tab[idx] : 0;
-    sum += v[e];
-  }
-  int run = wave_incl_sum(sum) - sum;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int idx = lane * per + e;
-    if (e < per && idx < n) tab[idx] = run;
-    run += v[e];
-  }
-}
-
-// Candidate keys of one (request, KV head).  Thread t owns blocks t + NT*j,
-// so every load instruction of a wavefront reads 256 contiguous bytes.  KPT > 0
-// keeps KPT rounds in registers, loaded before the request's length is known
-// (indices clamped into the row); KPT == 0 re-reads the row (any size).
+// Candidate keys of one (request, KV head).  KPT > 0: thread t owns the KPT
+// consecutive blocks [KPT t, KPT t + KPT), read with 16-byte loads before the
+// request's length is known (the row is padded to a multiple of 4 entries and
+// indices are clamped into it), so that a per-thread count and one scan give
+// every selected block its place in the ascending output.  KPT == 0 (any
+// size): thread t owns blocks t + NT j and re-reads the row.
 template <int NT, int KPT>
 struct KeyRuns {
+  static_assert(KPT % 4 == 0, "keys are read four at a time");
   uint32_t reg[KPT > 0 ? KPT : 1];
   const uint32_t* row;
   int C, rounds;
-  unsigned long long in_mask;  // KPT > 0: bit j set when this lane's key of round j is a candidate
-  __device__ void prefetch(const uint32_t* kr, int row_len) {
+  unsigned long long in_mask;  // KPT > 0: bit j set when this thread's key j is a candidate
+  __device__ void prefetch(const uint32_t* kr, int row_stride) {
     row = kr;
     if constexpr (KPT > 0) {
+      const uint4* r4 = reinterpret_cast<const uint4*>(kr);
+      const int last = row_stride / 4 - 1;
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const int idx = threadIdx.x + j * NT;
-        reg[j] = kr[idx < row_len ? idx : row_len - 1];
+      for (int v = 0; v < KPT / 4; ++v) {
+        const int idx = (int)threadIdx.x * (KPT / 4) + v;
+        const uint4 x = r4[idx < last ? idx : last];
+        reg[4 * v] = x.x;
+        reg[4 * v + 1] = x.y;
+        reg[4 * v + 2] = x.z;
+        reg[4 * v + 3] = x.w;
       }
     }
   }
   __device__ void set_count(int c) {
     C = c;
     rounds = (c + NT - 1) / NT;
-    const int mine = c > (int)threadIdx.x ? (c - (int)threadIdx.x + NT - 1) / NT : 0;  // rounds with a candidate
-    in_mask = mine >= 64 ? ~0ull : (1ull << mine) - 1ull;
+    if constexpr (KPT > 0) {
+      const int mine = min(max(c - (int)threadIdx.x * KPT, 0), KPT);  // candidates among this thread's keys
+      in_mask = mine >= 64 ? ~0ull : (1ull << mine) - 1ull;
+    }
   }
-  __device__ bool valid(int j) const { return j < rounds && (int)threadIdx.x + j * NT < C; }
+  __device__ bool valid(int j) const {
+    if constexpr (KPT > 0) return (in_mask >> j) & 1ull;
+    else return j < rounds && (int)threadIdx.x + j * NT < C;
+  }
   __device__ uint32_t key(int j) const {
     if constexpr (KPT > 0) return reg[j];
     else return row[threadIdx.x + j * NT];
@@ -486,28 +476,24 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
                                                    const int32_t* __restrict__ seq_lens,
                                                    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
                                                    int H, int max_blocks, int max_sel, int budget_num,
-                                                   int budget_den, int min_blocks, int local_blocks) {
+                                                   int budget_den, int min_blocks, int local_blocks,
+                                                   int key_stride) {
   constexpr int NW = NT / 64;
   constexpr int BPT = kBins / NT;                   // histogram bins per thread in the scan
-  constexpr int TAB = KPT > 0 ? NW * KPT : 1;       // per-(round, wavefront) table
   constexpr bool kKeepBins = KPT > 0 && KPT <= 16;  // first-pass bins kept in registers (16 bits each)
-  static_assert(TAB <= 512, "table scan covers at most 512 entries");
-  static_assert(KPT <= 64, "member mask holds one bit per round");
+  static_assert(KPT <= 64, "member mask holds one bit per key");
   __shared__ uint32_t hist2[2][kBins + 1];  // alternating pass histograms; the last slot takes non-members
   __shared__ int lds_waves[NW];
   __shared__ uint32_t lds_min[NW], lds_max[NW];
   __shared__ uint32_t bucket[kFinishMax];
-  __shared__ int tab[TAB];
   __shared__ int bc2[2][3];  // boundary record of a pass (bin, rank left, keys), by pass parity
   __shared__ int packed;      // keys of the boundary bucket packed so far
 
   const int i = blockIdx.x;
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   KeyRuns<NT, KPT> kr;
-  kr.prefetch(keys + ((size_t)r * H + i) * max_blocks, max_blocks);  // in flight with seq_lens
+  kr.prefetch(keys + ((size_t)r * H + i) * key_stride, key_stride);  // in flight with seq_lens
   const int L = clampi(seq_lens[r], 0, max_blocks * kBlock);
   const int M = (L + kBlock - 1) / kBlock;
   int32_t* out = sel_idx + ((size_t)r * H + i) * max_sel;
@@ -700,57 +686,29 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     n_eq = bucket_n;
   }
 
-  // Output in ascending block order.  Round j of wavefront w covers blocks
-  // [NT j + 64 w, NT j + 64 w + 64), so a table of per-(round, wavefront)
-  // ballot counts, scanned once, gives every wavefront's output offset and a
-  // lane prefix count places each block.
+  // Output in ascending block order.  Each thread's keys are consecutive
+  // blocks, so one scan of the per-thread counts gives every thread its first
+  // output position; ties at the threshold are ranked the same way.
   const bool ties = take_eq < n_eq;
   if constexpr (KPT > 0) {
-    int eq_rank_base[KPT];
-    if (ties) {
-      int counts = 0;
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const int c = __popcll(__ballot(kr.valid(j) && kr.key(j) == thr));
-        counts = lane == j ? c : counts;
-      }
-      if (lane < KPT) tab[lane * NW + wave] = counts;
-      __syncthreads();
-      if (wave == 0) wave_scan_table(tab, TAB);
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) eq_rank_base[j] = tab[j * NW + wave];
-      __syncthreads();
+    unsigned long long above = 0, equal = 0;
+    RESA_FOR_KEYS({
+      const uint32_t x = kr.key(j);
+      above |= (in && x > thr ? 1ull : 0ull) << j;
+      equal |= (in && x == thr ? 1ull : 0ull) << j;
+    });
+    unsigned long long take = above | equal;
+    if (ties) {  // of the keys equal to the threshold, the take_eq lowest block ids
+      int n_all;
+      int room = take_eq - block_exclusive_scan<NT>(__popcll(equal), lds_waves, n_all);
+      take = above;
+      for (unsigned long long m = equal; m != 0ull && room > 0; m &= m - 1ull, --room) take |= m & (~m + 1ull);
     }
-    bool take[KPT];
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) take[j] = false;
-    RESA_FOR_KEYS({ take[j] = in && kr.key(j) >= thr; });
-    if (ties) {
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const bool is_eq = kr.valid(j) && kr.key(j) == thr;
-        const unsigned long long m = __ballot(is_eq);
-        const int rank = eq_rank_base[j] + (int)lane_prefix(m);
-        if (is_eq) take[j] = rank < take_eq;
-      }
-    }
-    int counts = 0;  // lane j: this wavefront's count in round j
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int c = __popcll(__ballot(take[j]));  // ballot outside the lane select
-      counts = lane == j ? c : counts;
-    }
-    if (lane < KPT) tab[lane * NW + wave] = counts;
-    __syncthreads();
-    if (wave == 0) wave_scan_table(tab, TAB);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const unsigned long long m = __ballot(take[j]);
-      const int pos = tab[j * NW + wave] + (int)lane_prefix(m);
-      if (take[j] && pos < k) out[pos] = tid + j * NT;
-    }
+    int tot;
+    int pos = block_exclusive_scan<NT>(__popcll(take), lds_waves, tot);
+    const int first = tid * KPT;
+    for (unsigned long long m = take; m != 0ull; m &= m - 1ull, ++pos)
+      if (pos < k) out[pos] = first + __builtin_ctzll(m);
   } else {
     // Any number of rounds: one block scan per round.
     int base_out = 0, base_eq = 0;
@@ -784,7 +742,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
 #define RESA_SELECT_LAUNCH(NT, KPT)                                                                          \
   hipLaunchKernelGGL((select_kernel<NT, KPT>), grid, dim3(NT), 0, stream, a.keys, a.seq_lens, a.sel_idx,      \
                      a.sel_cnt, a.H, a.max_blocks, a.max_sel, a.budget_num, a.budget_den, a.min_blocks,      \
-                     a.local_blocks)
+                     a.local_blocks, a.key_stride)
   // 16 wavefronts: the select is latency-bound on one CU, and more resident
   // wavefronts hide more of it than fewer, longer ones (measured).
   if (cand_max <= 8LL * 1024) RESA_SELECT_LAUNCH(1024, 8);
