@@ -459,6 +459,13 @@ struct BinMap {
     return min(max(b, 0), kBins - 1);
   }
   __device__ int key_bin(uint32_t key) const { return (int)((min(max(key, lo), hi) - lo) >> shift); }
+  // The same maps for a key known to lie in [lo, hi] (no clamping on that
+  // side); any other key gives an unspecified bin.
+  __device__ int value_bin_in(uint32_t key) const {
+    const int b = (int)((__uint_as_float(u32_from_order_key(key)) - fmin) * scale);
+    return min(b, kBins - 1);
+  }
+  __device__ int key_bin_in(uint32_t key) const { return (int)((key - lo) >> shift); }
   __device__ int operator()(uint32_t key) const { return by_value ? value_bin(key) : key_bin(key); }
 };
 
@@ -577,8 +584,10 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
       else bins[j / 2] = kept;                                      \
     }                                                               \
   }
-      if (map.by_value) RESA_FOR_KEYS(RESA_COUNT_KEY(map.value_bin(kr.key(j))));
-      else RESA_FOR_KEYS(RESA_COUNT_KEY(map.key_bin(kr.key(j))));
+      // every candidate lies in [min, max] of the candidates; the bins of the
+      // others are not used
+      if (map.by_value) RESA_FOR_KEYS(RESA_COUNT_KEY(map.value_bin_in(kr.key(j))));
+      else RESA_FOR_KEYS(RESA_COUNT_KEY(map.key_bin_in(kr.key(j))));
 #undef RESA_COUNT_KEY
     } else {
       RESA_FOR_KEYS({
