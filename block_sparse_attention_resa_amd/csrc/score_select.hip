@@ -647,19 +647,37 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     // counts the members above and equal to it; the one whose rank range
     // holds `remaining` is the threshold.
     const bool kept = kKeepBins && npass == 1;
-    RESA_FOR_KEYS({
-      bool m;
-      if constexpr (kKeepBins) {
-        if (kept) m = (int)((bins[j / 2] >> (16 * (j & 1))) & 0xffffu) == bk.bin;  // non-candidates kept kBins
-        else m = in && bk.has(kr.key(j));
-      } else {
-        m = in && bk.has(kr.key(j));
+    if constexpr (KPT > 0) {
+      // members as a bit mask; only the few threads holding any claim slots
+      unsigned long long mem = 0;
+      RESA_FOR_KEYS({
+        bool m;
+        if constexpr (kKeepBins) {
+          if (kept) m = (int)((bins[j / 2] >> (16 * (j & 1))) & 0xffffu) == bk.bin;  // non-candidates kept kBins
+          else m = in && bk.has(kr.key(j));
+        } else {
+          m = in && bk.has(kr.key(j));
+        }
+        mem |= (m ? 1ull : 0ull) << j;
+      });
+      if (mem != 0ull) {
+        int pos = atomicAdd(&packed, __popcll(mem));
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          if ((mem >> j) & 1ull) {
+            if (pos < kFinishMax) bucket[pos] = kr.key(j);
+            ++pos;
+          }
+        }
       }
-      if (m) {
-        const int pos = atomicAdd(&packed, 1);
-        if (pos < kFinishMax) bucket[pos] = kr.key(j);
-      }
-    });
+    } else {
+      RESA_FOR_KEYS({
+        if (in && bk.has(kr.key(j))) {
+          const int pos = atomicAdd(&packed, 1);
+          if (pos < kFinishMax) bucket[pos] = kr.key(j);
+        }
+      });
+    }
     __syncthreads();
     const int nb = bucket_n;  // the members counted by the last pass
     int* bc = bc2[npass & 1];  // the record the last pass did not use
