@@ -28,7 +28,9 @@ __device__ __forceinline__ uint32_t bf16x2_from_order_key(ushort2_t k) {
   return __builtin_bit_cast(uint32_t, k ^ (~__builtin_bit_cast(ushort2_t, s) | (unsigned short)0x8000));
 }
 
-// Packed 16-bit min / max of two words.
+// Packed 16-bit min / max of two words.  The lane-swap results go through
+// these 32-bit helpers: written directly as vector min / max of the two
+// swap results, the operation was dropped from the generated code.
 __device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ushort2_t, a),
                                                                 __builtin_bit_cast(ushort2_t, b)));
