@@ -80,6 +80,31 @@ struct ChunkLoad<float> {
 
 constexpr int kScoreUnroll = 4;
 
+// Sum over aligned groups of N lanes, the result in every lane of the group.
+// N = 16 (a whole DPP row) and 32 use row rotations (and one 16-lane swap),
+// which stay in the vector ALU; other N use lane shuffles.
+template <int N>
+__device__ __forceinline__ float row_rot_add(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror:4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror:2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));  // row_ror:1
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N == 16) {
+    return row_rot_add<16>(x);
+  } else if constexpr (N == 32) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return row_rot_add<16>(__uint_as_float(a[0]) + __uint_as_float(a[1]));
+  } else {
+#pragma unroll
+    for (int off = N / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+  }
+}
+
 template <typename T, int D, int MODE, int MAXG>
 __global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, const T* desc,
                                                     const int32_t* __restrict__ table,
@@ -225,8 +250,7 @@ __global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, co
     float acc = 0.f;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) acc = fmaf(coef[v], vals[v], acc);
-#pragma unroll
-    for (int off = HALF; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    acc = group_sum<CH>(acc);
     if (lg == 0 && bl[u] < M) {
       key_row[bl[u]] = f32_order_key(acc);
       if (score_row) score_row[bl[u]] = acc;
