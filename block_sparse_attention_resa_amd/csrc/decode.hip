@@ -245,8 +245,8 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(
 // kMergeParts consecutive lanes share one output float4: lane part p folds
 // splits p, p + kMergeParts, p + 2 kMergeParts, ... in increasing order with
 // the running (m, l, o) update, all loads of a batch of kMergeBatch splits
-// issued before the first use; the partial states are then combined by lane
-// exchanges (xor 1, 2, 4, 8), each pair in the same order on both lanes.  No
+// issued before the first use; the partial states are then combined by DPP
+// lane exchanges, each pair in the same order on both lanes.  No
 // barrier and no LDS, and the order of every sum is fixed, so the result is
 // deterministic.
 constexpr int kMergeThreads = 256;
@@ -266,6 +266,29 @@ __device__ __forceinline__ void merge_into(MergeState& a, float m_s, float l_s, 
   a.l = a.l * wa + l_s * wb;
   a.o = a.o * wa + o_s * wb;
   a.m = m;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// One butterfly step of the merge: the partner's state arrives through the
+// DPP pattern CTRL; the lane whose part has bit OFF clear is the lower one.
+template <int CTRL, int OFF>
+__device__ __forceinline__ void combine_step(MergeState& st, int part) {
+  const float m_o = dpp_f32<CTRL>(st.m);
+  const float l_o = dpp_f32<CTRL>(st.l);
+  floatx4_t o_o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o_o[e] = dpp_f32<CTRL>(st.o[e]);
+  if ((part & OFF) == 0) {
+    merge_into(st, m_o, l_o, o_o);
+  } else {  // the same sum in the same order as the partner computes it
+    MergeState other{m_o, l_o, o_o};
+    merge_into(other, st.m, st.l, st.o);
+    st = other;
+  }
 }
 
 template <int D>
@@ -301,22 +324,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
 #pragma unroll
     for (int b = 0; b < kMergeBatch; ++b) merge_into(st, mv[b], lv[b], ov[b]);
   }
-  // combine the parts: xor 1, 2, 4, 8 (the lanes of one output are consecutive)
-#pragma unroll
-  for (int off = 1; off < kMergeParts; off <<= 1) {
-    const float m_o = __shfl_xor(st.m, off);
-    const float l_o = __shfl_xor(st.l, off);
-    floatx4_t o_o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o_o[e] = __shfl_xor(st.o[e], off);
-    if ((part & off) == 0) {
-      merge_into(st, m_o, l_o, o_o);
-    } else {  // the same sum in the same order as the partner computes it
-      MergeState other{m_o, l_o, o_o};
-      merge_into(other, st.m, st.l, st.o);
-      st = other;
-    }
-  }
+  // combine the parts (the sixteen lanes of one output are one DPP row):
+  // partners at xor 1 and xor 2 (quad permutes), then across quad pairs and
+  // half rows by mirroring, which pairs lanes of two groups that already hold
+  // equal states; both partners form the same sum in the same order.
+  combine_step<0xb1, 1>(st, part);   // quad_perm [1,0,3,2]
+  combine_step<0x4e, 2>(st, part);   // quad_perm [2,3,0,1]
+  combine_step<0x141, 4>(st, part);  // row_half_mirror
+  combine_step<0x140, 8>(st, part);  // row_mirror
   if (live && part == 0) {
     const int r = ri / H;
     const int i = ri % H;
