@@ -383,10 +383,12 @@ __device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, uint32
 template <int NT, int KPT>
 struct KeyRuns {
   static_assert(KPT % 4 == 0, "keys are read four at a time");
+  static_assert(KPT <= 32, "the member mask holds one bit per key");
   uint32_t reg[KPT > 0 ? KPT : 1];
   const uint32_t* row;
   int C, rounds;
-  unsigned long long in_mask;  // KPT > 0: bit j set when this thread's key j is a candidate
+  uint32_t in_mask;  // KPT > 0: bit j set when this thread's key j is a candidate
+  bool full;         // KPT > 0, uniform over the wavefront: every key of every lane is a candidate
   __device__ void prefetch(const uint32_t* kr, int row_stride) {
     row = kr;
     if constexpr (KPT > 0) {
@@ -408,11 +410,14 @@ struct KeyRuns {
     rounds = (c + NT - 1) / NT;
     if constexpr (KPT > 0) {
       const int mine = min(max(c - (int)threadIdx.x * KPT, 0), KPT);  // candidates among this thread's keys
-      in_mask = mine >= 64 ? ~0ull : (1ull << mine) - 1ull;
+      in_mask = mine >= 32 ? ~0u : (1u << mine) - 1u;
+      full = __all(mine == KPT) != 0;
+    } else {
+      full = false;
     }
   }
   __device__ bool valid(int j) const {
-    if constexpr (KPT > 0) return (in_mask >> j) & 1ull;
+    if constexpr (KPT > 0) return (in_mask >> j) & 1u;
     else return j < rounds && (int)threadIdx.x + j * NT < C;
   }
   __device__ uint32_t key(int j) const {
@@ -423,14 +428,26 @@ struct KeyRuns {
 };
 
 // Runs the statements in the variadic argument for every round j of `kr`,
-// with `in` telling whether the lane's key of that round is a candidate.
+// with `in` telling whether the lane's key of that round is a candidate.  In
+// wavefronts whose keys are all candidates (all but the last one or two of a
+// row) `in` is the constant true, so those run the statements unmasked.
 // Expects NT, KPT and a KeyRuns `kr` in scope.
 #define RESA_FOR_KEYS(...)                                                       \
   do {                                                                           \
     if constexpr (KPT > 0) {                                                     \
-      _Pragma("unroll") for (int j = 0; j < KPT; ++j) {                          \
-        const bool in = (kr.in_mask >> j) & 1ull;                                \
-        __VA_ARGS__                                                              \
+      if (kr.full) {                                                             \
+        _Pragma("unroll") for (int j = 0; j < KPT; ++j) {                        \
+          constexpr bool in = true;                                              \
+          __VA_ARGS__                                                            \
+        }                                                                        \
+      } else {                                                                   \
+        /* opaque copy: the per-key conditions are not kept across phases */    \
+        uint32_t im_ = kr.in_mask;                                               \
+        asm volatile("" : "+v"(im_));                                            \
+        _Pragma("unroll") for (int j = 0; j < KPT; ++j) {                        \
+          const bool in = (im_ >> j) & 1u;                                       \
+          __VA_ARGS__                                                            \
+        }                                                                        \
       }                                                                          \
     } else {                                                                     \
       for (int j = 0; j < kr.rounds; ++j) {                                      \
@@ -512,7 +529,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
   constexpr int NW = NT / 64;
   constexpr int BPT = kBins / NT;                   // histogram bins per thread in the scan
   constexpr bool kKeepBins = KPT > 0 && KPT <= 16;  // first-pass bins kept in registers (16 bits each)
-  static_assert(KPT <= 64, "member mask holds one bit per key");
+  static_assert(KPT <= 32, "member masks hold one bit per key");
   __shared__ uint32_t hist2[2][kBins + 1];  // alternating pass histograms; the last slot takes non-members
   __shared__ int lds_waves[NW];
   __shared__ uint32_t lds_min[NW], lds_max[NW];
@@ -600,10 +617,10 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     if (npass == 0) {  // every candidate is in the bucket
 #define RESA_COUNT_KEY(BIN)                                         \
   {                                                                 \
-    const int b = BIN;                                              \
-    if (in) atomicAdd(&hist[b], 1u);                                \
+    const int b = in ? (BIN) : kBins; /* spare slot */              \
+    atomicAdd(&hist[b], 1u);                                        \
     if constexpr (kKeepBins) {                                      \
-      const uint32_t kept = in ? (uint32_t)b : (uint32_t)kBins;     \
+      const uint32_t kept = (uint32_t)b;                            \
       if (j & 1) bins[j / 2] |= kept << 16;                         \
       else bins[j / 2] = kept;                                      \
     }                                                               \
@@ -673,7 +690,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     const bool kept = kKeepBins && npass == 1;
     if constexpr (KPT > 0) {
       // members as a bit mask; only the few threads holding any claim slots
-      unsigned long long mem = 0;
+      uint32_t mem = 0;
       RESA_FOR_KEYS({
         bool m;
         if constexpr (kKeepBins) {
@@ -682,13 +699,13 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
         } else {
           m = in && bk.has(kr.key(j));
         }
-        mem |= (m ? 1ull : 0ull) << j;
+        mem |= (m ? 1u : 0u) << j;
       });
-      if (mem != 0ull) {
-        int pos = atomicAdd(&packed, __popcll(mem));
+      if (mem != 0u) {
+        int pos = atomicAdd(&packed, __popc(mem));
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
-          if ((mem >> j) & 1ull) {
+          if ((mem >> j) & 1u) {
             if (pos < kFinishMax) bucket[pos] = kr.key(j);
             ++pos;
           }
@@ -742,24 +759,25 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
   // output position; ties at the threshold are ranked the same way.
   const bool ties = take_eq < n_eq;
   if constexpr (KPT > 0) {
-    unsigned long long above = 0, equal = 0;
-    RESA_FOR_KEYS({
-      const uint32_t x = kr.key(j);
-      above |= (in && x > thr ? 1ull : 0ull) << j;
-      equal |= (in && x == thr ? 1ull : 0ull) << j;
-    });
-    unsigned long long take = above | equal;
-    if (ties) {  // of the keys equal to the threshold, the take_eq lowest block ids
+    uint32_t take = 0;
+    if (!ties) {  // every key at or above the threshold
+      RESA_FOR_KEYS({ take |= (in && kr.key(j) >= thr ? 1u : 0u) << j; });
+    } else {  // of the keys equal to the threshold, the take_eq lowest block ids
+      uint32_t equal = 0;
+      RESA_FOR_KEYS({
+        const uint32_t x = kr.key(j);
+        take |= (in && x > thr ? 1u : 0u) << j;
+        equal |= (in && x == thr ? 1u : 0u) << j;
+      });
       int n_all;
-      int room = take_eq - block_exclusive_scan<NT>(__popcll(equal), lds_waves, n_all);
-      take = above;
-      for (unsigned long long m = equal; m != 0ull && room > 0; m &= m - 1ull, --room) take |= m & (~m + 1ull);
+      int room = take_eq - block_exclusive_scan<NT>(__popc(equal), lds_waves, n_all);
+      for (uint32_t m = equal; m != 0u && room > 0; m &= m - 1u, --room) take |= m & (~m + 1u);
     }
     int tot;
-    int pos = block_exclusive_scan<NT>(__popcll(take), lds_waves, tot);
+    int pos = block_exclusive_scan<NT>(__popc(take), lds_waves, tot);
     const int first = tid * KPT;
-    for (unsigned long long m = take; m != 0ull; m &= m - 1ull, ++pos)
-      if (pos < k) out[pos] = first + __builtin_ctzll(m);
+    for (uint32_t m = take; m != 0u; m &= m - 1u, ++pos)
+      if (pos < k) out[pos] = first + __builtin_ctz(m);
   } else {
     // Any number of rounds: one block scan per round.
     int base_out = 0, base_eq = 0;
