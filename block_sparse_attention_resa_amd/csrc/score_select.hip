@@ -689,25 +689,33 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     // holds `remaining` is the threshold.
     const bool kept = kKeepBins && npass == 1;
     if constexpr (KPT > 0) {
-      // members as a bit mask; only the few threads holding any claim slots
+      // members as a bit mask (after one pass, from the kept bins, where
+      // non-candidates hold kBins, which is no bucket's bin)
       uint32_t mem = 0;
-      RESA_FOR_KEYS({
-        bool m;
-        if constexpr (kKeepBins) {
-          if (kept) m = (int)((bins[j / 2] >> (16 * (j & 1))) & 0xffffu) == bk.bin;  // non-candidates kept kBins
-          else m = in && bk.has(kr.key(j));
-        } else {
-          m = in && bk.has(kr.key(j));
-        }
-        mem |= (m ? 1u : 0u) << j;
-      });
-      if (mem != 0u) {
-        int pos = atomicAdd(&packed, __popc(mem));
+      bool by_kept = false;
+      if constexpr (kKeepBins) by_kept = kept;
+      if (by_kept) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+          mem |= (((bins[j / 2] >> (16 * (j & 1))) & 0xffffu) == (uint32_t)bk.bin ? 1u : 0u) << j;
+      } else {
+        RESA_FOR_KEYS({ mem |= (in && bk.has(kr.key(j)) ? 1u : 0u) << j; });
+      }
+      // Slots: one LDS atomic per wavefront that holds members; each lane's
+      // members follow those of the lanes before it.  Keys of a round that
+      // holds no member in the wavefront are skipped as a whole.
+      if (__ballot(mem != 0u)) {
+        const int cnt = __popc(mem);
+        const int incl = wave_incl_sum(cnt);
+        int base = 0;
+        if ((tid & 63) == 63) base = atomicAdd(&packed, incl);
+        int pos = __builtin_amdgcn_readlane(base, 63) + incl - cnt;
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
-          if ((mem >> j) & 1u) {
-            if (pos < kFinishMax) bucket[pos] = kr.key(j);
-            ++pos;
+          const bool b = (mem >> j) & 1u;
+          if (__ballot(b)) {
+            if (b && pos < kFinishMax) bucket[pos] = kr.key(j);
+            pos += b ? 1 : 0;
           }
         }
       }
