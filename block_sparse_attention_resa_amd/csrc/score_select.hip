@@ -292,7 +292,8 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
 
 constexpr int kDigitBits = 11;  // histogram pass: 2048 bins
 constexpr int kBins = 1 << kDigitBits;
-constexpr int kFinishMax = 256;  // boundary bucket size the ranking finish takes
+constexpr int kFinishMax = 256;  // boundary bucket size the ranking finish takes (a multiple of 8)
+static_assert(kFinishMax % 8 == 0, "the ranking reads the bucket eight keys at a time");
 
 // Cross-lane steps through DPP (row shifts within 16-lane rows, then the
 // row-15 / row-31 broadcasts), which stay in the vector ALU instead of the
@@ -533,7 +534,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
   __shared__ uint32_t hist2[2][kBins + 1];  // alternating pass histograms; the last slot takes non-members
   __shared__ int lds_waves[NW];
   __shared__ uint32_t lds_min[NW], lds_max[NW];
-  __shared__ uint32_t bucket[kFinishMax];
+  __shared__ __align__(16) uint32_t bucket[kFinishMax];
   __shared__ int bc2[2][3];  // boundary record of a pass (bin, rank left, keys), by pass parity
   __shared__ int packed;      // keys of the boundary bucket packed so far
 
@@ -733,10 +734,18 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     if (tid < nb) {
       const uint32_t x = bucket[tid];
       int gt = 0, eq = 0;
-      for (int q = 0; q < nb; ++q) {
-        const uint32_t y = bucket[q];
-        gt += y > x ? 1 : 0;
-        eq += y == x ? 1 : 0;
+      // four members per LDS read, two reads in flight (slots past nb are masked)
+      const uint4* b4 = reinterpret_cast<const uint4*>(bucket);
+      for (int q = 0; q < nb; q += 8) {
+        const uint4 ya = b4[q / 4];
+        const uint4 yb = b4[q / 4 + 1];  // q + 7 < kFinishMax: kFinishMax is a multiple of 8
+        const uint32_t y[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool ok = q + e < nb;
+          gt += ok && y[e] > x ? 1 : 0;
+          eq += ok && y[e] == x ? 1 : 0;
+        }
       }
       if (gt < remaining && remaining <= gt + eq) {  // every writer stores the same values
         bc[0] = (int)x;
