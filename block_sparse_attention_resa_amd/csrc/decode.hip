@@ -242,53 +242,37 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(
 
 // Log-sum-exp merge of split partials:
 //   out[c] = sum_s 2^(m_s - m) o_s[c] / sum_s 2^(m_s - m) l_s,  m = max_s m_s.
-// kMergeParts consecutive lanes share one output float4: lane part p folds
-// splits p, p + kMergeParts, p + 2 kMergeParts, ... in increasing order with
-// the running (m, l, o) update, all loads of a batch of kMergeBatch splits
-// issued before the first use; the partial states are then combined by DPP
-// lane exchanges, each pair in the same order on both lanes.  No
-// barrier and no LDS, and the order of every sum is fixed, so the result is
-// deterministic.
+// kMergeParts consecutive lanes (one DPP row) share one output float4: lane
+// part p folds splits p, p + kMergeParts, p + 2 kMergeParts, ..., a batch of
+// kMergeBatch at a time with all loads issued first, each batch weighted
+// against its own maximum (independent exponentials rather than a chain).
+// The sixteen lanes then agree on the row maximum by DPP exchanges, scale
+// their sums once, and add them by DPP exchanges (partners at xor 1 and 2,
+// then the half-row and row mirrors, which pair lanes of groups already
+// holding equal values).  Floating-point addition is commutative, so both
+// partners of an exchange form the same value; with no barrier, no LDS and
+// a fixed order of every sum, the result is deterministic.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeParts = 16;  // lanes per output float4
 constexpr int kMergeBatch = 4;   // splits per lane per batch of loads
-
-struct MergeState {
-  float m, l;
-  floatx4_t o;
-};
-
-__device__ __forceinline__ void merge_into(MergeState& a, float m_s, float l_s, floatx4_t o_s) {
-  const float m = fmaxf(a.m, m_s);
-  if (m == -INFINITY) return;  // nothing seen on either side
-  const float wa = a.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(a.m - m);
-  const float wb = m_s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_s - m);
-  a.l = a.l * wa + l_s * wb;
-  a.o = a.o * wa + o_s * wb;
-  a.m = m;
-}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
-// One butterfly step of the merge: the partner's state arrives through the
-// DPP pattern CTRL; the lane whose part has bit OFF clear is the lower one.
-template <int CTRL, int OFF>
-__device__ __forceinline__ void combine_step(MergeState& st, int part) {
-  const float m_o = dpp_f32<CTRL>(st.m);
-  const float l_o = dpp_f32<CTRL>(st.l);
-  floatx4_t o_o;
+// Maximum, then sum, over the sixteen lanes of a DPP row.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f32<0xb1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f32<0x4e>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f32<0x141>(x));  // row_half_mirror
+  return fmaxf(x, dpp_f32<0x140>(x));  // row_mirror
+}
+template <int CTRL>
+__device__ __forceinline__ void row16_add_step(float& l, floatx4_t& o) {
+  l += dpp_f32<CTRL>(l);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o_o[e] = dpp_f32<CTRL>(st.o[e]);
-  if ((part & OFF) == 0) {
-    merge_into(st, m_o, l_o, o_o);
-  } else {  // the same sum in the same order as the partner computes it
-    MergeState other{m_o, l_o, o_o};
-    merge_into(other, st.m, st.l, st.o);
-    st = other;
-  }
+  for (int e = 0; e < 4; ++e) o[e] += dpp_f32<CTRL>(o[e]);
 }
 
 template <int D>
@@ -307,7 +291,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   const int ri = live ? grow / rows_per_head : 0;  // r * H + i
   const size_t base = (size_t)ri * S;
 
-  MergeState st{-INFINITY, 0.f, floatx4_t{0.f, 0.f, 0.f, 0.f}};
+  float m_run = -INFINITY, l_run = 0.f;
+  floatx4_t o_run = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = part; s0 < S; s0 += kMergeParts * kMergeBatch) {
     float mv[kMergeBatch], lv[kMergeBatch];
     floatx4_t ov[kMergeBatch];
@@ -321,25 +306,38 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
       lv[b] = ok ? ml.y : 0.f;
       ov[b] = *reinterpret_cast<const floatx4_t*>(part_o + pr * D + 4 * c4);
     }
+    float m_new = m_run;
 #pragma unroll
-    for (int b = 0; b < kMergeBatch; ++b) merge_into(st, mv[b], lv[b], ov[b]);
+    for (int b = 0; b < kMergeBatch; ++b) m_new = fmaxf(m_new, mv[b]);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // nothing seen yet: every weight is 0
+    const float a = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_use);
+    l_run *= a;
+    o_run *= a;
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) {
+      const float w = mv[b] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[b] - m_use);
+      l_run = fmaf(w, lv[b], l_run);
+      o_run += w * ov[b];
+    }
+    m_run = m_new;
   }
-  // combine the parts (the sixteen lanes of one output are one DPP row):
-  // partners at xor 1 and xor 2 (quad permutes), then across quad pairs and
-  // half rows by mirroring, which pairs lanes of two groups that already hold
-  // equal states; both partners form the same sum in the same order.
-  combine_step<0xb1, 1>(st, part);   // quad_perm [1,0,3,2]
-  combine_step<0x4e, 2>(st, part);   // quad_perm [2,3,0,1]
-  combine_step<0x141, 4>(st, part);  // row_half_mirror
-  combine_step<0x140, 8>(st, part);  // row_mirror
+  const float m_all = row16_max(m_run);
+  const float m_use = m_all == -INFINITY ? 0.f : m_all;
+  const float w = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_use);
+  float l_sum = l_run * w;
+  floatx4_t o_sum = o_run * w;
+  row16_add_step<0xb1>(l_sum, o_sum);
+  row16_add_step<0x4e>(l_sum, o_sum);
+  row16_add_step<0x141>(l_sum, o_sum);
+  row16_add_step<0x140>(l_sum, o_sum);
   if (live && part == 0) {
     const int r = ri / H;
     const int i = ri % H;
     const int j = row % G;
     const int t = row / G;
     float* dst = out + (((size_t)r * row_stride_out + t) * H * G + (size_t)i * G + j) * D + 4 * c4;
-    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-    *reinterpret_cast<floatx4_t*>(dst) = st.o * inv;
+    const float inv = l_sum > 0.f ? 1.f / l_sum : 0.f;
+    *reinterpret_cast<floatx4_t*>(dst) = o_sum * inv;
   }
 }
 
