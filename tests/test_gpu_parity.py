@@ -220,6 +220,32 @@ def test_split_count_changes_rounding_only():
     assert torch.equal(a, b), "dense decode not bitwise deterministic"
 
 
+def test_many_splits_merge_batches():
+    """More splits than one lane group folds in one batch of loads (64), so the
+    merge runs several batches; dense and all-blocks sparse decode against the
+    oracle's dense attention."""
+    case = make("bf16_d64_h2_g3")  # 5000 rows: 313 blocks
+    M = num_blocks(case.inp.seq_lens[0])
+    g = case.spec.group_size
+    scale = C.sm_scale(case.cfg)
+    refs = {}
+    for i in range(case.spec.num_kv_heads):
+        refs[i] = O.dense(C.group_q(case, 0, i), C.keys_of(case, 0, i), C.values_of(case, 0, i),
+                          case.inp.seq_lens[0], scale)
+    idx = torch.full((1, case.spec.num_kv_heads, M), -1, dtype=torch.int32, device="cuda")
+    idx[0, :, :] = torch.arange(M, dtype=torch.int32, device="cuda")
+    cnt = torch.full((1, case.spec.num_kv_heads), M, dtype=torch.int32, device="cuda")
+    for S in (65, 129, 200, M):
+        case.cfg.num_splits = S
+        de = C.run_dense(case)
+        sp = C.run_sparse(case, idx, cnt)
+        torch.cuda.synchronize()
+        for i in range(case.spec.num_kv_heads):
+            C.check_out(de[0, i * g:(i + 1) * g].cpu().numpy(), refs[i], f"dense S={S} i{i}")
+            C.check_out(sp[0, i * g:(i + 1) * g].cpu().numpy(), refs[i], f"sparse all-blocks S={S} i{i}")
+    case.cfg.num_splits = 0
+
+
 def test_zero_length_request():
     spec = BF.with_(num_requests=2, seq_lens=(33, 700))
     case = C.make_case(spec, 5)
