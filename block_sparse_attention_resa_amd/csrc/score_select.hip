@@ -12,7 +12,8 @@
 // the group's queries into its own slice of (P, N) once and the kernel then
 // streams the descriptors with one fused multiply-add per stored value.  A
 // descriptor (2 x d values) is split into 32-byte chunks; CH consecutive
-// lanes own one descriptor and combine their partial sums with shuffles.
+// lanes own one descriptor and combine their partial sums with DPP row
+// rotations.
 // The thread -> (KV head, chunk) assignment is fixed for the whole kernel so
 // the coefficients stay in registers.  Scores are written as order-preserving
 // 32-bit keys for the selection kernel.
@@ -28,7 +29,8 @@
 // are packed into LDS and ranked in parallel.  Blocks above the threshold
 // are taken, blocks equal to it lowest index first, and one scan of the
 // per-thread counts places every selected id in ascending order.
-// Wave-wide scans and reductions use DPP lane shifts.
+// Wave-wide scans and reductions use DPP lane shifts, and wavefronts whose
+// keys are all candidates run every per-key loop without masks.
 #include "desc_unit.h"
 #include "resa_internal.h"
 
