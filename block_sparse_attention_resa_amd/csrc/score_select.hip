@@ -392,6 +392,7 @@ struct KeyRuns {
   int C, rounds;
   uint32_t in_mask;  // KPT > 0: bit j set when this thread's key j is a candidate
   bool full;         // KPT > 0, uniform over the wavefront: every key of every lane is a candidate
+  bool any;          // KPT > 0, uniform over the wavefront: some lane holds a candidate
   __device__ void prefetch(const uint32_t* kr, int row_stride) {
     row = kr;
     if constexpr (KPT > 0) {
@@ -415,8 +416,10 @@ struct KeyRuns {
       const int mine = min(max(c - (int)threadIdx.x * KPT, 0), KPT);  // candidates among this thread's keys
       in_mask = mine >= 32 ? ~0u : (1u << mine) - 1u;
       full = __all(mine == KPT) != 0;
+      any = __any(mine > 0) != 0;
     } else {
       full = false;
+      any = true;
     }
   }
   __device__ bool valid(int j) const {
@@ -433,8 +436,9 @@ struct KeyRuns {
 // Runs the statements in the variadic argument for every round j of `kr`,
 // with `in` telling whether the lane's key of that round is a candidate.  In
 // wavefronts whose keys are all candidates (all but the last one or two of a
-// row) `in` is the constant true, so those run the statements unmasked.
-// Expects NT, KPT and a KeyRuns `kr` in scope.
+// row) `in` is the constant true, so those run the statements unmasked;
+// wavefronts without a candidate skip them (every use is a no-op for a key
+// that is not a candidate).  Expects NT, KPT and a KeyRuns `kr` in scope.
 #define RESA_FOR_KEYS(...)                                                       \
   do {                                                                           \
     if constexpr (KPT > 0) {                                                     \
@@ -443,7 +447,7 @@ struct KeyRuns {
           constexpr bool in = true;                                              \
           __VA_ARGS__                                                            \
         }                                                                        \
-      } else {                                                                   \
+      } else if (kr.any) {                                                       \
         /* opaque copy: the per-key conditions are not kept across phases */    \
         uint32_t im_ = kr.in_mask;                                               \
         asm volatile("" : "+v"(im_));                                            \
@@ -596,6 +600,8 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
   int remaining = k;  // keys still to take from the bucket
   int bucket_n = C;   // keys in the bucket
   uint32_t bins[kKeepBins ? KPT / 2 : 1];  // first-pass bin of every key, two per register
+#pragma unroll
+  for (int v = 0; v < (kKeepBins ? KPT / 2 : 1); ++v) bins[v] = (uint32_t)kBins | ((uint32_t)kBins << 16);
 
   // Histogram passes until the bucket holding the k-th largest key is small.
   int npass = 0;
@@ -620,10 +626,10 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     if (npass == 0) {  // every candidate is in the bucket
 #define RESA_COUNT_KEY(BIN)                                         \
   {                                                                 \
-    const int b = in ? (BIN) : kBins; /* spare slot */              \
-    atomicAdd(&hist[b], 1u);                                        \
+    const int b = BIN;                                              \
+    if (in) atomicAdd(&hist[b], 1u); /* constant in full waves */   \
     if constexpr (kKeepBins) {                                      \
-      const uint32_t kept = (uint32_t)b;                            \
+      const uint32_t kept = in ? (uint32_t)b : (uint32_t)kBins;     \
       if (j & 1) bins[j / 2] |= kept << 16;                         \
       else bins[j / 2] = kept;                                      \
     }                                                               \
