@@ -150,10 +150,13 @@ __global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, co
   uint32_t* key_row = keys + ((size_t)r * H + head) * key_stride;
   float* score_row = scores ? scores + ((size_t)r * H + head) * max_blocks : nullptr;
 
-  // Physical ids of this workgroup's blocks: one coalesced load per wavefront
-  // (all table columns are in bounds), handed to the lanes with a shuffle.
-  // Blocks past the sequence end are dropped at the end, so no address here
-  // waits for seq_lens.
+  // The request length (a scalar load) and the physical ids of this
+  // workgroup's blocks (one coalesced load per wavefront, handed to the lanes
+  // with a shuffle) are in flight together; the descriptor loads need both,
+  // so skipping blocks past the sequence end costs no extra wait and no
+  // descriptor past it is read (in a ragged batch the table is sized for the
+  // longest request).
+  const int seq_len = seq_lens[r];  // first used after the query loads are issued
   int my_pid = 0;
   if (lane < wg_blocks && wg_b0 + lane < max_blocks) my_pid = table[(size_t)r * max_blocks + wg_b0 + lane];
   // Load order matters: the in-order vector-memory counter makes a wait for
@@ -178,6 +181,8 @@ __global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, co
 #pragma unroll
     for (int j = 0; j < kMaxG; ++j) qv[j] = *reinterpret_cast<const Pair*>(qh + (size_t)min(j, G - 1) * D);
   }
+  const int L = clampi(seq_len, 0, max_blocks * kBlock);
+  const int M = (L + kBlock - 1) / kBlock;
   uint4 buf[kScoreUnroll][2];
   int bl[kScoreUnroll];
 #pragma unroll
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, co
     const int b = wg_b0 + bo;
     bl[u] = b;
     const int p = clampi(__shfl(my_pid, bo), 0, num_pool_blocks - 1);
-    if (b < max_blocks) {
+    if (b < M) {
       const uint4* src = reinterpret_cast<const uint4*>(desc + (((size_t)p * H + head) * 2 + part) * D + c0);
       buf[u][0] = src[0];
       buf[u][1] = src[1];
@@ -243,8 +248,6 @@ __global__ __launch_bounds__(1024) void score_kernel(const T* __restrict__ q, co
     coef[v + 3] = c4[3];
   }
 
-  const int L = clampi(seq_lens[r], 0, max_blocks * kBlock);
-  const int M = (L + kBlock - 1) / kBlock;
 #pragma unroll
   for (int u = 0; u < kScoreUnroll; ++u) {
     float vals[VPL];
