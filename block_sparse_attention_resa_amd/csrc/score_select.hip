@@ -338,12 +338,24 @@ __device__ __forceinline__ void wave_min_max(uint32_t& mn, uint32_t& mx) {
   mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
 }
 
+// Cross-wavefront exchange slots, two sets used alternately: a call writes
+// its set, waits at one barrier and reads it; the next call of the same kind
+// writes the other set, and the call after that can rewrite the first only
+// after every thread has passed the intervening call's barrier, i.e. after
+// every read of the first call.  So one barrier per call suffices.
+template <typename V, int NW>
+struct WaveSlots {
+  V v[2][NW];
+};
+
 // Exclusive prefix sum over the workgroup in thread order; `total` gets the sum.
 template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& total) {
+__device__ __forceinline__ int block_exclusive_scan(int v, WaveSlots<int, NT / 64>& slots, int& use, int& total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  int* lds_waves = slots.v[use];
+  use ^= 1;
   const int incl = wave_incl_sum(v);
   if (lane == 63) lds_waves[wave] = incl;
   __syncthreads();
@@ -355,29 +367,28 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_waves, int& 
     before += w < wave ? x : 0;
     total += x;
   }
-  __syncthreads();
   return before + incl - v;
 }
 
 template <int NT>
-__device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, uint32_t* lds_min, uint32_t* lds_max) {
+__device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, WaveSlots<uint2, NT / 64>& slots,
+                                              int& use) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  uint2* lds_mm = slots.v[use];
+  use ^= 1;
   wave_min_max(mn, mx);
-  if (lane == 0) {
-    lds_min[wave] = mn;
-    lds_max[wave] = mx;
-  }
+  if (lane == 0) lds_mm[wave] = make_uint2(mn, mx);
   __syncthreads();
   mn = 0xffffffffu;
   mx = 0u;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    mn = min(mn, lds_min[w]);
-    mx = max(mx, lds_max[w]);
+    const uint2 x = lds_mm[w];
+    mn = min(mn, x.x);
+    mx = max(mx, x.y);
   }
-  __syncthreads();  // lds_min / lds_max may be rewritten right after
 }
 
 // Candidate keys of one (request, KV head).  KPT > 0: thread t owns the KPT
@@ -541,8 +552,9 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
   constexpr bool kKeepBins = KPT > 0 && KPT <= 16;  // first-pass bins kept in registers (16 bits each)
   static_assert(KPT <= 32, "member masks hold one bit per key");
   __shared__ uint32_t hist2[2][kBins + 1];  // alternating pass histograms; the last slot takes non-members
-  __shared__ int lds_waves[NW];
-  __shared__ uint32_t lds_min[NW], lds_max[NW];
+  __shared__ WaveSlots<int, NW> scan_slots;
+  __shared__ WaveSlots<uint2, NW> mm_slots;
+  int scan_use = 0, mm_use = 0;  // alternating slot sets, identical in every thread
   __shared__ __align__(16) uint32_t bucket[kFinishMax];
   __shared__ int bc2[2][3];  // boundary record of a pass (bin, rank left, keys), by pass parity
   __shared__ int packed;      // keys of the boundary bucket packed so far
@@ -593,7 +605,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
     mn = in ? min(mn, x) : mn;
     mx = in ? max(mx, x) : mx;
   });
-  block_min_max<NT>(mn, mx, lds_min, lds_max);
+  block_min_max<NT>(mn, mx, mm_slots, mm_use);
 
   Bucket bk;
   bk.lo = mn;
@@ -617,7 +629,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
         a = m ? min(a, x) : a;
         b = m ? max(b, x) : b;
       });
-      block_min_max<NT>(a, b, lds_min, lds_max);
+      block_min_max<NT>(a, b, mm_slots, mm_use);
       bk.lo = a;
       bk.hi = b;
       bk.bin = -1;
@@ -660,7 +672,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
       c += (int)hb[e];
     }
     int tot;
-    const int above0 = block_exclusive_scan<NT>(c, lds_waves, tot);
+    const int above0 = block_exclusive_scan<NT>(c, scan_slots, scan_use, tot);
     int* bc = bc2[npass & 1];
     // this pass's histogram is read; clear it for the pass after next
 #pragma unroll
@@ -776,7 +788,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
       const uint32_t x = kr.key(j);
       a = (in && bk.has(x)) ? min(a, x) : a;
     });
-    block_min_max<NT>(a, b, lds_min, lds_max);
+    block_min_max<NT>(a, b, mm_slots, mm_use);
     thr = a;
     take_eq = bucket_n;
     n_eq = bucket_n;
@@ -798,11 +810,11 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
         equal |= (in && x == thr ? 1u : 0u) << j;
       });
       int n_all;
-      int room = take_eq - block_exclusive_scan<NT>(__popc(equal), lds_waves, n_all);
+      int room = take_eq - block_exclusive_scan<NT>(__popc(equal), scan_slots, scan_use, n_all);
       for (uint32_t m = equal; m != 0u && room > 0; m &= m - 1u, --room) take |= m & (~m + 1u);
     }
     int tot;
-    int pos = block_exclusive_scan<NT>(__popc(take), lds_waves, tot);
+    int pos = block_exclusive_scan<NT>(__popc(take), scan_slots, scan_use, tot);
     const int first = tid * KPT;
     for (uint32_t m = take; m != 0u; m &= m - 1u, ++pos)
       if (pos < k) out[pos] = first + __builtin_ctz(m);
@@ -814,10 +826,10 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
       const uint32_t x = kr.key(j);
       const bool is_eq = v && x == thr;
       int tot_eq;
-      const int eq_before = block_exclusive_scan<NT>(is_eq ? 1 : 0, lds_waves, tot_eq);
+      const int eq_before = block_exclusive_scan<NT>(is_eq ? 1 : 0, scan_slots, scan_use, tot_eq);
       const bool t = (v && x > thr) || (is_eq && (!ties || base_eq + eq_before < take_eq));
       int tot;
-      const int pos = block_exclusive_scan<NT>(t ? 1 : 0, lds_waves, tot);
+      const int pos = block_exclusive_scan<NT>(t ? 1 : 0, scan_slots, scan_use, tot);
       if (t && base_out + pos < k) out[base_out + pos] = tid + j * NT;
       base_out += tot;
       base_eq += tot_eq;
