@@ -316,3 +316,28 @@ def test_rectify_parity(name):
             # descriptors of every block equal a rebuild of the rewritten cache
             C.check_descriptors(case, r, i, K2, L)
             C.check_out(out[r, :, i * g:(i + 1) * g].cpu().numpy(), ref, f"{name} r{r} i{i}")
+
+
+def test_rectify_long_split_fallback_kernel():
+    """A caller-forced single split longer than the LDS kernel's page-id list
+    (2048 blocks) takes the direct-load kernel; both kernels against the oracle."""
+    spec = BF.with_(num_kv_heads=1, seq_lens=(16 * 2100 + 9,))
+    chunk = 32
+    outs = {}
+    for S in (1, 0):
+        case = C.make_case(spec, 31)
+        case.cfg.num_splits = S
+        C.run_descriptors(case)
+        qc, kn, vn = make_rectify_inputs(spec, 31, chunk, device="cuda")
+        K0, V0 = C.logical_cache(case)
+        out = torch.full((1, chunk, spec.group_size * 1, spec.head_dim), float("nan"), device="cuda")
+        ws = resa.alloc_workspace(case.cfg, resa.OP_DENSE_RECTIFY, 1, case.kv.max_blocks, chunk=chunk)
+        resa.dense_rectify(case.cfg, case.kv, qc, kn, vn, out, ws)
+        torch.cuda.synchronize()
+        outs[S] = out
+        L = case.inp.seq_lens[0]
+        ref, K2, V2, tb, lo, hi = O.rectify(C.np64(qc[0]), C.np64(kn[0, :, 0]), C.np64(vn[0, :, 0]),
+                                            C.np64(K0[0][0]), C.np64(V0[0][0]), L, C.sm_scale(case.cfg))
+        C.check_descriptors(case, 0, 0, K2, L)
+        C.check_out(out[0].cpu().numpy(), ref, f"rectify splits={S}")
+    assert resa.num_splits(case.cfg, resa.OP_DENSE_RECTIFY, 1, case.kv.max_blocks, 0, chunk) > 1
