@@ -341,3 +341,60 @@ def test_rectify_long_split_fallback_kernel():
         C.check_descriptors(case, 0, 0, K2, L)
         C.check_out(out[0].cpu().numpy(), ref, f"rectify splits={S}")
     assert resa.num_splits(case.cfg, resa.OP_DENSE_RECTIFY, 1, case.kv.max_blocks, 0, chunk) > 1
+
+
+def test_out_of_range_device_values_are_clamped():
+    """Values read from device memory are clamped into range (the conventions
+    in include/resa.h): a sequence length past the table's capacity acts as the
+    capacity and a negative one as 0, block-table entries outside the pool act
+    as the nearest pool block, selected ids outside the table as the nearest
+    column and a count past the list as the list.  Each run with out-of-range
+    values must equal, bit for bit, the run with the clamped values."""
+    import dataclasses
+
+    case = make("bf16_d128_L647")
+    C.run_descriptors(case)
+    kv = case.kv
+    P, mb = int(kv.k_pool.shape[0]), kv.max_blocks
+
+    def with_kv(table=None, seq=None):
+        return dataclasses.replace(case, kv=resa.PagedKV(kv.k_pool, kv.v_pool, kv.desc_pool,
+                                                          kv.block_table if table is None else table,
+                                                          kv.seq_lens if seq is None else seq))
+
+    def all_outputs(c):
+        sel, cnt, sc = C.run_score_select(c)
+        sp = C.run_sparse(c, sel, cnt)
+        de = C.run_dense(c)
+        torch.cuda.synchronize()
+        return [sel, cnt, sc, sp, de]
+
+    def same(a, b, tag):
+        for x, y in zip(a, b):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), tag
+
+    def seq(v):
+        return torch.tensor([v], dtype=torch.int32, device="cuda")
+
+    same(all_outputs(with_kv(seq=seq(2 ** 30))), all_outputs(with_kv(seq=seq(mb * 16))), "long sequence length")
+    neg = all_outputs(with_kv(seq=seq(-5)))
+    same(neg, all_outputs(with_kv(seq=seq(0))), "negative sequence length")
+    assert int(neg[1].abs().sum()) == 0 and float(neg[4].abs().max()) == 0.0
+
+    bad, clamped = kv.block_table.clone(), kv.block_table.clone()
+    bad[0, 3], clamped[0, 3] = -7, 0
+    bad[0, 5], clamped[0, 5] = P + 1000, P - 1
+    same(all_outputs(with_kv(table=bad)), all_outputs(with_kv(table=clamped)), "block-table entries")
+
+    sel, cnt, _ = C.run_score_select(case)
+    M = num_blocks(case.inp.seq_lens[0])
+    ms = sel.shape[2]
+    sel_bad, sel_c = sel.clone(), sel.clone()
+    sel_bad[0, 0, 1], sel_c[0, 0, 1] = -4, 0
+    sel_bad[0, 0, 2], sel_c[0, 0, 2] = mb + 9, mb - 1
+    cnt_bad, cnt_c = cnt.clone(), cnt.clone()
+    cnt_bad[0, 1], cnt_c[0, 1] = ms + 50, min(ms, M)
+    a = C.run_sparse(case, sel_bad, cnt_bad)
+    b = C.run_sparse(case, sel_c, cnt_c)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "selected ids and counts"
