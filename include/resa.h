@@ -72,7 +72,7 @@ extern "C" {
 typedef enum {
   RESA_OK = 0,
   RESA_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shape */
-  RESA_ERR_UNSUPPORTED = 2, /* a configuration this build has no kernel for */
+  RESA_ERR_UNSUPPORTED = 2, /* a configuration the library has no kernel for */
   RESA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
   RESA_ERR_LAUNCH = 4       /* a kernel launch failed */
 } resa_status;
