@@ -69,17 +69,18 @@ def source_hash(*names):
 
 
 def measured_traffic(kernel_hash):
-    """HBM bytes per launch of the sparse decode kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    """HBM bytes per launch of the sparse decode call and the kernel-trace
+    durations of its two kernels, from the committed rocprofv3 summary, if it
+    was taken on the current kernel source (else (None, None))."""
     path = os.path.join(ROOT, "profiles", "sparse_decode_traffic_256k.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     if rec.get("kernel_source_hash") != kernel_hash:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return None, None
+    return rec.get("hbm_bytes_per_launch"), rec.get("rocprof_avg_us")
 
 
 def main(argv=None):
@@ -251,7 +252,7 @@ def main(argv=None):
     dec_bytes = ab["kv"] + ab["q"] + ab["out"]
     dec_gbps = dec_bytes / (t_dec * 1e-6) / 1e9
     khash = source_hash("decode.hip", "attn_frag.h", "resa_internal.h")
-    traffic = measured_traffic(khash)
+    traffic, trace_us = measured_traffic(khash)
 
     # ---------------------------------------------------------------- check + CPU oracle
     cpu = None
@@ -353,7 +354,7 @@ def main(argv=None):
                      "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": dec_bytes, "avg_launch_us": round(t_dec, 3),
-                     "kernel_source_hash": khash},
+                     "trace_avg_us": trace_us, "kernel_source_hash": khash},
         "cpu_baseline": cpu,
         "oracle_check_max_abs_err": check,
     }
