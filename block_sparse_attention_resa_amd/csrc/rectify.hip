@@ -16,8 +16,9 @@
 //      head are the columns of 16-wide MFMA tiles.  bf16 caches: a 512-thread
 //      workgroup holds sixteen tiles (256 query rows) and streams one split
 //      of the cache through LDS, so every K / V byte is read from HBM once
-//      per workgroup.  fp32 caches: a 256-thread workgroup holds four tiles
-//      and each wavefront reads its K / V operands directly.  Each query row
+//      per workgroup.  fp32 caches (and bf16 splits longer than the 2048
+//      page ids the LDS kernel keeps): a 256-thread workgroup holds four
+//      tiles and each wavefront reads its K / V operands directly.  Each query row
 //      t masks positions > L - chunk + t; blocks past the workgroup's last
 //      visible position are skipped;
 //   4. the log-sum-exp merge of the splits (shared with decode).
