@@ -60,6 +60,16 @@ def algorithmic_bytes(spec, L, n_sel, e):
     return {"desc": desc, "kv": kv, "q": q, "out": out, "total": desc + kv + q + out}
 
 
+def layers_for_fresh_reads(spec, lens, e=2):
+    """Number of independent layer caches a timed replay cycles through so
+    that the bytes one replay touches (descriptors + selected K/V, at the
+    default 10 % budget) exceed 1 GiB, four times the 256 MB last-level
+    cache: every step then reads its data from HBM, as in a model whose other
+    layers' traffic evicts it between steps.  Between 2 and 256 caches."""
+    touched = sum(algorithmic_bytes(spec, L, max(16, -(-((L + 15) // 16) // 10)), e)["total"] for L in lens)
+    return max(2, min(256, -(-(1 << 30) // touched)))
+
+
 def source_hash(*names):
     h = hashlib.sha256()
     for n in names:
@@ -371,8 +381,9 @@ def sweep(args):
     refresh + sparse decode) for contexts 16K / 64K / 256K, budgets
     2 / 5 / 10 / 20 % and both scoring modes at 10 %, next to the dense decode
     and the rectification of a 32-token window.  Every figure is a HIP-graph
-    replay over several layer caches (at least 1 GiB in all, so nothing is
-    served from the 256 MB last-level cache), divided by the layer count;
+    replay over enough layer caches that one replay touches more than 1 GiB
+    (so nothing is served from the 256 MB last-level cache), divided by the
+    layer count;
     the two calls of the step are also timed alone.  Printed as a markdown
     table."""
     import torch
@@ -407,8 +418,7 @@ def sweep(args):
         return (time.perf_counter() - t0) * 1e6 / steps / n_items
 
     for L in SWEEP_CTX:
-        layer_bytes = 2 * H * L * d * 2
-        nl = max(2, min(16, -(-(1 << 30) // layer_bytes)))  # >= 1 GiB of caches: no reuse from the 256 MB cache
+        nl = layers_for_fresh_reads(base, [L])
         spec = base.with_(seq_lens=(L,), layers=nl, name=f"ctx{L}")
         caches = []
         for l in range(nl):
@@ -500,8 +510,9 @@ def workloads(args):
     fraction of 8 TB/s, the dense decode and the speedup, and the
     rectification of the workload's window (the rectify workload's f, else
     32) with its useful TFLOP/s and fraction of the 2.5 PFLOP/s bf16 MFMA
-    peak.  HIP-graph replays over several layer caches (at least 1 GiB in
-    all), divided by the layer count.  Printed as a markdown table."""
+    peak.  HIP-graph replays over enough layer caches that one replay
+    touches more than 1 GiB (no reuse from the last-level cache), divided by
+    the layer count.  Printed as a markdown table."""
     import torch
 
     import block_sparse_attention_resa_amd as resa
@@ -542,8 +553,7 @@ def workloads(args):
             inp = make_layer(spec, seed=SEED, layer=l, device="cuda")
             lens = list(inp.seq_lens)
             if l == 0:
-                layer_bytes = sum(2 * H * L * d * e for L in lens)
-                nl = max(2, min(16, -(-(1 << 30) // layer_bytes)))
+                nl = layers_for_fresh_reads(spec, lens, e)
             pg = make_paged(inp)
             kv = resa.PagedKV(pg.k_pool, pg.v_pool, pg.desc_pool, pg.block_table, pg.seq_lens)
             resa.build_descriptors(cfg, kv)
