@@ -105,6 +105,9 @@ def main(argv=None):
                     help="also run one plain device copy of this size (HBM counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line: context x budget x scoring-mode table (markdown)")
+    ap.add_argument("--cycle", action="store_true",
+                    help="instead of the headline line: the decoding loop at 256K (32 sparse steps at growing "
+                         "lengths, then the rectification of the last 32 positions, per layer), amortised")
     ap.add_argument("--workloads", action="store_true",
                     help="instead of the headline line: every bf16 workload (batch, ragged, 131K + rectify) "
                          "as a markdown table")
@@ -130,6 +133,8 @@ def main(argv=None):
         return sweep(args)
     if args.workloads:
         return workloads(args)
+    if args.cycle:
+        return cycle(args)
     spec = WORKLOADS[args.workload]
     assert spec.num_requests == 1 and spec.dtype == "bf16"
     L = spec.seq_lens[0]
@@ -496,6 +501,113 @@ def sweep(args):
         print(f"| {r['ctx']} | {r['budget']} | {r['mode']} | {r['n_sel']} | {r['us_step']:.1f} | "
               f"{r['us_score_select']:.1f} | {r['us_decode']:.1f} | {r['gbps']:.0f} | {r['us_dense']:.1f} | "
               f"{r['speedup']:.2f} | {r['us_rectify_f32']:.0f} | {r['cycle_speedup']:.2f} |")
+    return 0
+
+
+CYCLE_F = 32  # rectification window and period (the analysis page's default f)
+
+
+def cycle(args):
+    """The decoding loop of Algorithm 1 at 256K, timed end to end: for each of
+    the 28 layers, CYCLE_F sparse steps at sequence lengths L - f + 1 ... L
+    (score/select with the tail-descriptor refresh + sparse decode; the rows
+    of those positions are already in the cache), then the rectification of
+    the last f positions (row write, descriptor refresh, causal chunk
+    attention).  Steps run layer by layer within each step, the
+    rectification pass after the f-th step, all captured once in a HIP graph.
+    Prints one JSON line: microseconds per layer-step amortised over the
+    cycle, next to the dense decode per layer-step on the same caches."""
+    import torch
+
+    import block_sparse_attention_resa_amd as resa
+    from synth import WORKLOADS, make_layer, make_paged
+
+    spec = WORKLOADS["qwen7b_ctx256k_l28"]
+    L = spec.seq_lens[0]
+    H, g, d = spec.num_kv_heads, spec.group_size, spec.head_dim
+    f = CYCLE_F
+    cfg = resa.Config(num_kv_heads=H, group_size=g, head_dim=d, dtype=resa.RESA_BF16)
+    layers = []
+    for l in range(spec.layers):
+        inp = make_layer(spec, seed=SEED, layer=l, device="cuda")
+        pg = make_paged(inp)
+        kv = resa.PagedKV(pg.k_pool, pg.v_pool, pg.desc_pool, pg.block_table, pg.seq_lens)
+        resa.build_descriptors(cfg, kv)
+        # one view per step: the same pools and table, the step's sequence length
+        steps = [resa.PagedKV(pg.k_pool, pg.v_pool, pg.desc_pool, pg.block_table,
+                              torch.tensor([L - f + 1 + t], dtype=torch.int32, device="cuda")) for t in range(f)]
+        layers.append({"kv": kv, "steps": steps, "q": inp.q})
+        del inp
+    torch.cuda.synchronize()
+    log(f"cycle: {len(layers)} layer caches, f = {f}")
+    mb = layers[0]["kv"].max_blocks
+    ms = resa.selection_count(cfg, mb)
+    sel_idx = torch.empty((1, H, ms), dtype=torch.int32, device="cuda")
+    sel_cnt = torch.empty((1, H), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, H * g, d), device="cuda")
+    ws_s = resa.alloc_workspace(cfg, resa.OP_SCORE_SELECT, 1, mb, ms)
+    ws_d = resa.alloc_workspace(cfg, resa.OP_SPARSE_DECODE, 1, mb, ms)
+    ws_n = resa.alloc_workspace(cfg, resa.OP_DENSE_DECODE, 1, mb)
+    ws_r = resa.alloc_workspace(cfg, resa.OP_DENSE_RECTIFY, 1, mb, chunk=f)
+    gen = torch.Generator(device="cuda").manual_seed(SEED)
+    qc = torch.randn((1, f, H * g, d), device="cuda", generator=gen).to(torch.bfloat16)
+    kn = torch.randn((1, f, H, d), device="cuda", generator=gen).to(torch.bfloat16)
+    vn = torch.randn((1, f, H, d), device="cuda", generator=gen).to(torch.bfloat16)
+    rout = torch.empty((1, f, H * g, d), device="cuda")
+
+    def one_cycle():
+        for t in range(f):
+            for st in layers:
+                kv_t = st["steps"][t]
+                resa.score_select(cfg, kv_t, st["q"], sel_idx, sel_cnt, ws_s, refresh_tail=True)
+                resa.sparse_decode(cfg, kv_t, st["q"], sel_idx, sel_cnt, out, ws_d)
+        for st in layers:
+            resa.dense_rectify(cfg, st["kv"], qc, kn, vn, rout, ws_r)
+
+    def dense_step():
+        for st in layers:
+            resa.dense_decode(cfg, st["kv"], st["q"], out, ws_n)
+
+    def graph_of(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        torch.cuda.synchronize()
+        return gr
+
+    def replay_ms(gr, n):
+        gr.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            gr.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    gc = graph_of(one_cycle)
+    ms_cycle = replay_ms(gc, 5)
+    del gc
+    gd = graph_of(dense_step)
+    ms_dense = replay_ms(gd, 10)
+    del gd
+    nl = len(layers)
+    us_cycle = ms_cycle * 1e3 / (f * nl)
+    us_dense = ms_dense * 1e3 / nl
+    line = {"metric": "decode-loop us/layer-step incl. rectification every 32 steps, 256K ctx",
+            "value": round(us_cycle, 3), "unit": "us/layer-step", "n_gpus": 1, "higher_is_better": False,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "qwen7b_ctx256k_l28", "layers": nl, "f": f,
+                       "cycle": f"{f} sparse steps at lengths L-{f - 1}..L (score/select with tail refresh + "
+                                f"sparse decode) then rectification of the last {f} positions, per layer, HIP graph"},
+            "ms_per_cycle": round(ms_cycle, 3), "dense_us_per_layer_step": round(us_dense, 3),
+            "speedup_vs_dense": round(us_dense / us_cycle, 3)}
+    print(json.dumps(line), flush=True)
     return 0
 
 
