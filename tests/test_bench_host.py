@@ -36,3 +36,14 @@ def test_more_than_one_gpu_is_refused():
                        stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=300)
     assert p.returncode != 0
     assert "one GPU" in (p.stdout + p.stderr)
+
+
+def test_tables_read_fresh_data():
+    """The sweep and workload tables cycle through enough layer caches that
+    one replay touches more than 1 GiB, four times the last-level cache."""
+    base = WORKLOADS["qwen7b_ctx256k_l28"]
+    for L in (16384, 65536, 262144):
+        nl = bench.layers_for_fresh_reads(base, [L])
+        n = max(16, -(-((L + 15) // 16) // 10))
+        assert nl * bench.algorithmic_bytes(base, L, n, 2)["total"] >= 1 << 30
+        assert 2 <= nl <= 256
