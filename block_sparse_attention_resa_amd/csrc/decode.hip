@@ -255,6 +255,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(
 constexpr int kMergeThreads = 256;
 constexpr int kMergeParts = 16;  // lanes per output float4
 constexpr int kMergeBatch = 4;   // splits per lane per batch of loads
+constexpr long long kMergeMaxGrid = 1 << 20;  // workgroups of one merge launch
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -276,19 +277,15 @@ __device__ __forceinline__ void row16_add_step(float& l, floatx4_t& o) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part_o,
-                                                              const float* __restrict__ part_ml,
-                                                              float* __restrict__ out, int H, int G, int S,
-                                                              int rows_per_head, int row_stride_out,
-                                                              int total_rows) {
-  constexpr int C4 = D / 4;  // float4 per output row
-  const int g = blockIdx.x * kMergeThreads + threadIdx.x;
-  const int part = g % kMergeParts;
-  const int c4 = (g / kMergeParts) % C4;
-  const int grow = g / (kMergeParts * C4);  // (r, i, row) flattened
-  const bool live = grow < total_rows;
-  const int row = live ? grow % rows_per_head : 0;
-  const int ri = live ? grow / rows_per_head : 0;  // r * H + i
+__device__ __forceinline__ void merge_one(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                          float* __restrict__ out, int H, int G, int S, int rows_per_head,
+                                          int row_stride_out, long long g) {
+  constexpr int C4 = D / 4;
+  const int part = (int)(g % kMergeParts);
+  const int c4 = (int)((g / kMergeParts) % C4);
+  const long long grow = g / (kMergeParts * C4);  // (r, i, row) flattened
+  const int row = (int)(grow % rows_per_head);
+  const long long ri = grow / rows_per_head;  // r * H + i
   const size_t base = (size_t)ri * S;
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -299,7 +296,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
 #pragma unroll
     for (int b = 0; b < kMergeBatch; ++b) {
       const int sp = s0 + b * kMergeParts;
-      const bool ok = live && sp < S;
+      const bool ok = sp < S;
       const size_t pr = (base + (ok ? sp : 0)) * rows_per_head + row;
       const float2 ml = *reinterpret_cast<const float2*>(part_ml + pr * 2);
       mv[b] = ok ? ml.x : -INFINITY;
@@ -330,15 +327,32 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   row16_add_step<0x4e>(l_sum, o_sum);
   row16_add_step<0x141>(l_sum, o_sum);
   row16_add_step<0x140>(l_sum, o_sum);
-  if (live && part == 0) {
-    const int r = ri / H;
-    const int i = ri % H;
+  if (part == 0) {
+    const long long r = ri / H;
+    const int i = (int)(ri % H);
     const int j = row % G;
     const int t = row / G;
     float* dst = out + (((size_t)r * row_stride_out + t) * H * G + (size_t)i * G + j) * D + 4 * c4;
     const float inv = l_sum > 0.f ? 1.f / l_sum : 0.f;
     *reinterpret_cast<floatx4_t*>(dst) = o_sum * inv;
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part_o,
+                                                              const float* __restrict__ part_ml,
+                                                              float* __restrict__ out, int H, int G, int S,
+                                                              int rows_per_head, int row_stride_out,
+                                                              long long total_rows) {
+  constexpr int C4 = D / 4;  // float4 per output row
+  // 64-bit thread index; the grid strides over the rows when it is capped
+  // (rows * C4 * kMergeParts may exceed 2^31).  The stride is a multiple of
+  // kMergeParts, so the sixteen lanes of a DPP row always share one row and
+  // leave the loop together.
+  const long long stride = (long long)gridDim.x * kMergeThreads;
+  for (long long g = (long long)blockIdx.x * kMergeThreads + threadIdx.x; g < total_rows * C4 * kMergeParts;
+       g += stride)
+    merge_one<D>(part_o, part_ml, out, H, G, S, rows_per_head, row_stride_out, g);
 }
 
 template <typename T, int D, int NW>
@@ -367,13 +381,15 @@ hipError_t launch_merge(const float* part_o, const float* part_ml, float* out, i
                         int rows_per_head, int row_stride_out, hipStream_t stream) {
   const long long rows = (long long)R * H * rows_per_head;
   const long long threads = rows * (D / 4) * kMergeParts;
-  const dim3 grid((unsigned)((threads + kMergeThreads - 1) / kMergeThreads));
+  long long wgs = (threads + kMergeThreads - 1) / kMergeThreads;
+  if (wgs > kMergeMaxGrid) wgs = kMergeMaxGrid;  // larger merges stride over the rows
+  const dim3 grid((unsigned)wgs);
   if (D == 128)
     hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(kMergeThreads), 0, stream, part_o, part_ml, out, H, G, S,
-                       rows_per_head, row_stride_out, (int)rows);
+                       rows_per_head, row_stride_out, rows);
   else
     hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(kMergeThreads), 0, stream, part_o, part_ml, out, H, G, S,
-                       rows_per_head, row_stride_out, (int)rows);
+                       rows_per_head, row_stride_out, rows);
   return hipGetLastError();
 }
 
