@@ -29,5 +29,7 @@ from ._binding import (  # noqa: F401
     score_select,
     selection_count,
     sparse_decode,
+    sparse_decode_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     workspace_bytes,
 )

@@ -3,6 +3,9 @@
 // anything is enqueued; nothing here allocates, synchronises or prints.
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/resa.h"
 #include "resa_internal.h"
 
@@ -134,6 +137,40 @@ size_t workspace_bytes(const resa_config* c, int op, int R, int max_blocks, int 
 float scale_log2(const resa_config* c) { return (float)((double)c->sm_scale * 1.4426950408889634); }
 
 resa_status from_hip(hipError_t e) { return e == hipSuccess ? RESA_OK : RESA_ERR_LAUNCH; }
+
+constexpr int kMaxDevices = 64;  // devices whose scratch address is remembered
+
+}  // namespace
+
+// Device memory of resa_sparse_decode_noalloc: every GPU the library runs on
+// holds its own copy until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it uses the device address looked up by scratch_of_current_device.
+static __device__ __align__(256) unsigned char scratch[RESA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and remembered.
+resa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return RESA_ERR_LAUNCH;
+  if (dev >= kMaxDevices) return RESA_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RESA_ERR_LAUNCH;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return RESA_OK;
+}
 
 }  // namespace
 
@@ -319,6 +356,26 @@ resa_status resa_sparse_decode(const resa_config* cfg, const resa_paged_kv* kv, 
                                size_t ws_bytes, void* stream) {
   return decode_common(cfg, kv, num_requests, q, sel_idx, sel_cnt, max_sel, out, ws, ws_bytes, stream,
                        RESA_OP_SPARSE_DECODE);
+}
+
+resa_status resa_sparse_decode_noalloc(const resa_config* cfg, const resa_paged_kv* kv, int32_t num_requests,
+                                       const void* q, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                       int32_t max_sel, float* out, void* stream) {
+  // The same checks and kernels as resa_sparse_decode; the workspace is this
+  // device's static scratch, so a call needing more than its size is refused
+  // before anything is looked up or enqueued.
+  resa_status st = check_config(cfg);
+  if (st == RESA_OK) st = check_kv(kv, true, true, false);
+  if (st == RESA_OK) st = check_requests(num_requests);
+  if (st != RESA_OK) return st;
+  if (max_sel < 1) return RESA_ERR_INVALID_ARG;
+  const size_t need = workspace_bytes(cfg, RESA_OP_SPARSE_DECODE, num_requests, kv->max_blocks, max_sel, 0);
+  if (need > (size_t)RESA_NOALLOC_SCRATCH_BYTES) return RESA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != RESA_OK) return st;
+  return decode_common(cfg, kv, num_requests, q, sel_idx, sel_cnt, max_sel, out, ws,
+                       (size_t)RESA_NOALLOC_SCRATCH_BYTES, stream, RESA_OP_SPARSE_DECODE);
 }
 
 resa_status resa_dense_decode(const resa_config* cfg, const resa_paged_kv* kv, int32_t num_requests, const void* q,

@@ -207,6 +207,30 @@ resa_status resa_sparse_decode(const resa_config* cfg, const resa_paged_kv* kv,
                                size_t ws_bytes, void* stream);
 
 /*
+ * resa_sparse_decode without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid allocation.  It computes exactly what
+ * resa_sparse_decode computes, with the same kernels and the same argument
+ * checks.  Its workspace is a static device array of
+ * RESA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it
+ * runs on until the process ends; its address is looked up (once per device,
+ * with that device current) on the first call on a device.  The call
+ * allocates nothing: no hipMalloc, hipFree or allocating library routine.
+ * A call whose workspace (resa_workspace_bytes(cfg, RESA_OP_SPARSE_DECODE,
+ * num_requests, kv->max_blocks, max_sel, 0)) exceeds that size returns
+ * RESA_ERR_WORKSPACE and enqueues nothing.  All calls on one GPU share its
+ * array and it keeps the last call's contents (every call leaves the words
+ * that must start at zero at zero): calls that overlap on one GPU (on
+ * different streams, or from several threads) race and must be ordered by
+ * the caller.  A failed lookup of the array returns RESA_ERR_LAUNCH.
+ */
+#define RESA_NOALLOC_SCRATCH_BYTES (8u << 20)
+resa_status resa_sparse_decode_noalloc(const resa_config* cfg, const resa_paged_kv* kv,
+                                       int32_t num_requests, const void* q, const int32_t* sel_idx,
+                                       const int32_t* sel_cnt, int32_t max_sel, float* out,
+                                       void* stream);
+
+/*
  * Dense decode attention (Eq 1): as resa_sparse_decode with every block
  * [0, M) of every request.  The baseline of §5.  out is [R][H*g][d] float32.
  */

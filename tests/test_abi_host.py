@@ -207,3 +207,18 @@ def test_binding_rejects_cpu_tensors():
                    torch.zeros(1, 4, dtype=torch.int32), torch.zeros(1, dtype=torch.int32))
     with pytest.raises(ValueError):
         B.build_descriptors(cfgp, kv)
+
+
+def test_noalloc_refuses_more_than_its_scratch_before_any_gpu_call(lib):
+    """The no-allocation decode checks its size on the host: a call that
+    needs more than the static scratch returns the workspace error without
+    looking up the scratch or launching anything (fake pointers here)."""
+    c = cfg()
+    c.num_splits = 1024
+    kv = B.CPagedKV(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 40)
+    need = lib.resa_workspace_bytes(ctypes.byref(c), B.OP_SPARSE_DECODE, 1, 40, 2048, 0)
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    st = lib.resa_sparse_decode_noalloc(ctypes.byref(c), ctypes.byref(kv), 1, FAKE, FAKE, FAKE, 2048, FAKE, None)
+    assert st == 3
+    assert lib.resa_sparse_decode_noalloc(ctypes.byref(c), ctypes.byref(kv), 1, FAKE, FAKE, FAKE, 0, FAKE, None) == 1
+    assert lib.resa_sparse_decode_noalloc(None, ctypes.byref(kv), 1, FAKE, FAKE, FAKE, 16, FAKE, None) == 1
