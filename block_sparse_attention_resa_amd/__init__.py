@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     OP_DENSE_RECTIFY,
     OP_SCORE_SELECT,
     OP_SPARSE_DECODE,
+    OP_SPARSE_STEP,
     RESA_BF16,
     RESA_F32,
     RESA_SCORE_MEAN_POOL,
@@ -30,6 +31,7 @@ from ._binding import (  # noqa: F401
     selection_count,
     sparse_decode,
     sparse_decode_noalloc,
+    sparse_step,
     NOALLOC_SCRATCH_BYTES,
     workspace_bytes,
 )

@@ -31,11 +31,13 @@ OP_SCORE_SELECT = 1
 OP_SPARSE_DECODE = 2
 OP_DENSE_DECODE = 3
 OP_DENSE_RECTIFY = 4
+OP_SPARSE_STEP = 5
 
 EXPORTED = (
     "resa_abi_version", "resa_status_string", "resa_config_init", "resa_selection_count",
     "resa_workspace_bytes", "resa_num_splits", "resa_build_descriptors", "resa_score_select",
     "resa_sparse_decode", "resa_dense_decode", "resa_dense_rectify", "resa_sparse_decode_noalloc",
+    "resa_sparse_step",
 )
 
 NOALLOC_SCRATCH_BYTES = 8 << 20  # RESA_NOALLOC_SCRATCH_BYTES
@@ -89,6 +91,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "resa_score_select": (i32, [cfgp, kvp, i32, vp, i32, vp, vp, i32, vp, vp, sz, vp]),
         "resa_sparse_decode": (i32, [cfgp, kvp, i32, vp, vp, vp, i32, vp, vp, sz, vp]),
         "resa_sparse_decode_noalloc": (i32, [cfgp, kvp, i32, vp, vp, vp, i32, vp, vp]),
+        "resa_sparse_step": (i32, [cfgp, kvp, i32, vp, i32, vp, vp, i32, vp, vp, sz, vp]),
         "resa_dense_decode": (i32, [cfgp, kvp, i32, vp, vp, vp, sz, vp]),
         "resa_dense_rectify": (i32, [cfgp, kvp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
     }
@@ -265,6 +268,24 @@ def sparse_decode(cfg: Config, kv: PagedKV, q: torch.Tensor, sel_idx: torch.Tens
     _call("resa_sparse_decode", ctypes.byref(c), ctypes.byref(k), R, q.data_ptr(), sel_idx.data_ptr(),
           sel_cnt.data_ptr(), int(sel_idx.shape[2]), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
           _stream_ptr())
+
+
+def sparse_step(cfg: Config, kv: PagedKV, q: torch.Tensor, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
+                out: torch.Tensor, workspace: torch.Tensor, refresh_tail: bool = False) -> None:
+    """resa_score_select + resa_sparse_decode as one launch (workspace of OP_SPARSE_STEP, zeroed)."""
+    _check_cache(cfg, kv)
+    R, H, G, d = kv.num_requests, cfg.num_kv_heads, cfg.group_size, cfg.head_dim
+    _need(q, "q", cfg.torch_dtype, (R, H * G, d))
+    _need(sel_idx, "sel_idx", torch.int32)
+    if sel_idx.dim() != 3 or tuple(sel_idx.shape[:2]) != (R, H):
+        raise ValueError("sel_idx must be [R, H, max_sel]")
+    _need(sel_cnt, "sel_cnt", torch.int32, (R, H))
+    _need(out, "out", torch.float32, (R, H * G, d))
+    _need(workspace, "workspace", torch.uint8)
+    c, k = cfg.c(), kv.c()
+    _call("resa_sparse_step", ctypes.byref(c), ctypes.byref(k), R, q.data_ptr(), int(bool(refresh_tail)),
+          sel_idx.data_ptr(), sel_cnt.data_ptr(), int(sel_idx.shape[2]), out.data_ptr(), workspace.data_ptr(),
+          workspace.numel(), _stream_ptr())
 
 
 def sparse_decode_noalloc(cfg: Config, kv: PagedKV, q: torch.Tensor, sel_idx: torch.Tensor,

@@ -33,9 +33,6 @@ resa_status check_config(const resa_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return RESA_ERR_UNSUPPORTED;
   if (c->group_size > 16) return RESA_ERR_UNSUPPORTED;  // one 16-column MFMA tile per KV head
   if (c->num_kv_heads > 65535) return RESA_ERR_UNSUPPORTED;
-  // the score kernel keeps one descriptor-chunk lane group per KV head resident
-  const int lanes_per_desc = c->dtype == RESA_BF16 ? c->head_dim / 8 : c->head_dim / 4;
-  if ((long long)lanes_per_desc * c->num_kv_heads > 1024) return RESA_ERR_UNSUPPORTED;
   return RESA_OK;
 }
 
@@ -118,8 +115,10 @@ size_t partial_bytes(const resa_config* c, int R, int S, long long rows_per_head
 
 size_t workspace_bytes(const resa_config* c, int op, int R, int max_blocks, int max_sel, int chunk) {
   switch (op) {
-    case RESA_OP_SCORE_SELECT:
-      return align_up((size_t)R * c->num_kv_heads * key_stride_for(max_blocks) * sizeof(uint32_t));
+    case RESA_OP_SCORE_SELECT:  // arrival counters, slice key ranges, then the score keys
+      return align_up(score_select_sync_bytes(R, c->num_kv_heads)) +
+             align_up(score_select_range_bytes(R, c->num_kv_heads, max_blocks)) +
+             align_up((size_t)R * c->num_kv_heads * key_stride_for(max_blocks) * sizeof(uint32_t));
     case RESA_OP_SPARSE_DECODE:
     case RESA_OP_DENSE_DECODE: {
       const int S = splits_for(c, op, R, max_blocks, max_sel, chunk);
@@ -128,6 +127,13 @@ size_t workspace_bytes(const resa_config* c, int op, int R, int max_blocks, int 
     case RESA_OP_DENSE_RECTIFY: {
       const int S = splits_for(c, op, R, max_blocks, max_sel, chunk);
       return partial_bytes(c, R, S, (long long)chunk * c->group_size);
+    }
+    case RESA_OP_SPARSE_STEP: {
+      size_t parts[6];
+      step_workspace_parts(c->dtype, c->head_dim, R, c->num_kv_heads, c->group_size, max_blocks, max_sel, parts);
+      size_t total = 0;
+      for (size_t b : parts) total += align_up(b);
+      return total;
     }
     default:
       return 0;
@@ -221,7 +227,7 @@ size_t resa_workspace_bytes(const resa_config* cfg, int32_t op, int32_t num_requ
                             int32_t max_sel, int32_t chunk) {
   if (check_config(cfg) != RESA_OK || num_requests < 0 || max_blocks < 1 || max_blocks > kMaxBlocksLimit)
     return 0;
-  if (op == RESA_OP_SPARSE_DECODE && max_sel < 1) return 0;
+  if ((op == RESA_OP_SPARSE_DECODE || op == RESA_OP_SPARSE_STEP) && max_sel < 1) return 0;
   if (op == RESA_OP_DENSE_RECTIFY && (chunk < 1 || chunk > kMaxChunk)) return 0;
   return workspace_bytes(cfg, op, num_requests, max_blocks, max_sel, chunk);
 }
@@ -273,7 +279,6 @@ resa_status resa_score_select(const resa_config* cfg, const resa_paged_kv* kv, i
   const size_t need = workspace_bytes(cfg, RESA_OP_SCORE_SELECT, num_requests, kv->max_blocks, max_sel, 0);
   if (!ws || ws_bytes < need || !aligned16(ws)) return RESA_ERR_WORKSPACE;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   ScoreArgs sa{};
   sa.q = q;
@@ -282,8 +287,14 @@ resa_status resa_score_select(const resa_config* cfg, const resa_paged_kv* kv, i
   sa.refresh_tail = refresh_tail != 0;
   sa.table = kv->block_table;
   sa.seq_lens = kv->seq_lens;
-  sa.keys = static_cast<uint32_t*>(ws);
+  const size_t sync_b = align_up(score_select_sync_bytes(num_requests, cfg->num_kv_heads));
+  const size_t range_b = align_up(score_select_range_bytes(num_requests, cfg->num_kv_heads, kv->max_blocks));
+  sa.sync = static_cast<uint32_t*>(ws);
+  sa.ranges = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sync_b);
+  sa.keys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sync_b + range_b);
   sa.scores = scores;
+  sa.sel_idx = sel_idx;
+  sa.sel_cnt = sel_cnt;
   sa.R = num_requests;
   sa.H = cfg->num_kv_heads;
   sa.G = cfg->group_size;
@@ -293,23 +304,12 @@ resa_status resa_score_select(const resa_config* cfg, const resa_paged_kv* kv, i
   sa.num_pool_blocks = kv->num_pool_blocks;
   sa.mode = cfg->score_mode;
   sa.key_stride = key_stride_for(kv->max_blocks);
-  hipError_t e = launch_scores(sa, s);
-  if (e != hipSuccess) return RESA_ERR_LAUNCH;
-  SelectArgs se{};
-  se.keys = sa.keys;
-  se.seq_lens = kv->seq_lens;
-  se.sel_idx = sel_idx;
-  se.sel_cnt = sel_cnt;
-  se.R = num_requests;
-  se.H = cfg->num_kv_heads;
-  se.max_blocks = kv->max_blocks;
-  se.max_sel = max_sel;
-  se.budget_num = cfg->budget_num;
-  se.budget_den = cfg->budget_den;
-  se.min_blocks = cfg->min_blocks;
-  se.local_blocks = cfg->local_blocks;
-  se.key_stride = sa.key_stride;
-  return from_hip(launch_select(se, s));
+  sa.max_sel = max_sel;
+  sa.budget_num = cfg->budget_num;
+  sa.budget_den = cfg->budget_den;
+  sa.min_blocks = cfg->min_blocks;
+  sa.local_blocks = cfg->local_blocks;
+  return from_hip(launch_score_select(sa, static_cast<hipStream_t>(stream)));
 }
 
 static resa_status decode_common(const resa_config* cfg, const resa_paged_kv* kv, int32_t R, const void* q,
@@ -376,6 +376,74 @@ resa_status resa_sparse_decode_noalloc(const resa_config* cfg, const resa_paged_
   if (st != RESA_OK) return st;
   return decode_common(cfg, kv, num_requests, q, sel_idx, sel_cnt, max_sel, out, ws,
                        (size_t)RESA_NOALLOC_SCRATCH_BYTES, stream, RESA_OP_SPARSE_DECODE);
+}
+
+resa_status resa_sparse_step(const resa_config* cfg, const resa_paged_kv* kv, int32_t num_requests, const void* q,
+                             int32_t refresh_tail, int32_t* sel_idx, int32_t* sel_cnt, int32_t max_sel, float* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  resa_status st = check_config(cfg);
+  if (st == RESA_OK) st = check_kv(kv, true, true, true);
+  if (st == RESA_OK) st = check_requests(num_requests);
+  if (st != RESA_OK) return st;
+  if (!q || !aligned16(q) || !sel_idx || !sel_cnt || !out || !aligned16(out)) return RESA_ERR_INVALID_ARG;
+  if (max_sel < selection_count(cfg, kv->max_blocks)) return RESA_ERR_INVALID_ARG;
+  if (num_requests == 0) return RESA_OK;
+  const size_t need = workspace_bytes(cfg, RESA_OP_SPARSE_STEP, num_requests, kv->max_blocks, max_sel, 0);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return RESA_ERR_WORKSPACE;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return RESA_ERR_LAUNCH;
+  StepArgs a{};
+  a.q = q;
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.desc_pool = kv->desc_pool;
+  a.table = kv->block_table;
+  a.seq_lens = kv->seq_lens;
+  a.refresh_tail = refresh_tail != 0;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.out = out;
+  size_t parts[6];
+  step_workspace_parts(cfg->dtype, cfg->head_dim, num_requests, cfg->num_kv_heads, cfg->group_size, kv->max_blocks,
+                       max_sel, parts);
+  char* base = static_cast<char*>(ws);
+  size_t off = 0;
+  void* ptr[6];
+  for (int k = 0; k < 6; ++k) {
+    ptr[k] = base + off;
+    off += align_up(parts[k]);
+  }
+  a.flags = static_cast<uint32_t*>(ptr[0]);
+  a.stats = static_cast<uint32_t*>(ptr[1]);
+  a.keys = static_cast<uint32_t*>(ptr[2]);
+  a.unc = static_cast<uint32_t*>(ptr[3]);
+  a.part_o = static_cast<float*>(ptr[4]);
+  a.part_ml = static_cast<float*>(ptr[5]);
+  a.R = num_requests;
+  a.H = cfg->num_kv_heads;
+  a.G = cfg->group_size;
+  a.D = cfg->head_dim;
+  a.dtype = cfg->dtype;
+  a.max_blocks = kv->max_blocks;
+  a.num_pool_blocks = kv->num_pool_blocks;
+  a.mode = cfg->score_mode;
+  a.key_stride = key_stride_for(kv->max_blocks);
+  a.max_sel = max_sel;
+  a.budget_num = cfg->budget_num;
+  a.budget_den = cfg->budget_den;
+  a.min_blocks = cfg->min_blocks;
+  a.local_blocks = cfg->local_blocks;
+  a.scale_log2 = scale_log2(cfg);
+  step_geometry(cfg->dtype, cfg->head_dim, num_requests, cfg->num_kv_heads, kv->max_blocks, &a.unroll, &a.nslices);
+  // one workgroup per compute unit at most: every workgroup of the grid is
+  // resident at once, which the waits of the attention phase rely on
+  const long long units = (long long)num_requests * cfg->num_kv_heads * a.nslices;
+  if (units > 0x7fffffffLL) return RESA_ERR_UNSUPPORTED;
+  a.grid = (int)(units < cus ? units : cus);
+  (void)hipGetLastError();
+  return from_hip(launch_step(a, static_cast<hipStream_t>(stream)));
 }
 
 resa_status resa_dense_decode(const resa_config* cfg, const resa_paged_kv* kv, int32_t num_requests, const void* q,

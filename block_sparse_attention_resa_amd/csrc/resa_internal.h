@@ -69,34 +69,64 @@ struct DescArgs {
 };
 hipError_t launch_descriptors(const DescArgs& a, hipStream_t stream);
 
+// Scoring and selection of resa_score_select (one launch).
 struct ScoreArgs {
   const void* q;
-  const void* desc_pool;
-  const void* k_pool;  // read when refresh_tail
+  const void* desc_pool;  // also written (tail block) when refresh_tail
+  const void* k_pool;     // read when refresh_tail
   int32_t refresh_tail;
   const int32_t* table;
   const int32_t* seq_lens;
+  uint32_t* sync;    // [R][H] arrival counters (128-byte lines), zero between calls
+  uint32_t* ranges;  // [R][H][range_stride] per-slice key ranges
   uint32_t* keys;  // [R][H][key_stride] workspace
   float* scores;   // nullable export [R][H][max_blocks]
+  int32_t* sel_idx;
+  int32_t* sel_cnt;
   int32_t R, H, G, D, dtype, max_blocks, num_pool_blocks, mode;
   int32_t key_stride;  // key_stride_for(max_blocks)
+  int32_t max_sel, budget_num, budget_den, min_blocks, local_blocks;
+  int32_t nslices, unroll, range_stride;  // set by the launcher
 };
-hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream);
+hipError_t launch_score_select(const ScoreArgs& a, hipStream_t stream);
+// Bytes of the arrival counters of R x H rows (zero between calls) and of
+// their per-slice key ranges.
+size_t score_select_sync_bytes(int R, int H);
+size_t score_select_range_bytes(int R, int H, int max_blocks);
 
 // Row stride of the score keys: a multiple of 4 entries, so every row starts
 // 16-byte aligned and the selection can read its keys with 16-byte loads.
 inline int key_stride_for(int max_blocks) { return (max_blocks + 3) & ~3; }
 
-struct SelectArgs {
-  const uint32_t* keys;  // [R][H][key_stride]
+// One decode step of one layer (resa_sparse_step) in one persistent launch.
+struct StepArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  void* desc_pool;  // read; the tail block's descriptor written when refresh_tail
+  const int32_t* table;
   const int32_t* seq_lens;
+  int32_t refresh_tail;
   int32_t* sel_idx;
   int32_t* sel_cnt;
-  int32_t R, H, max_blocks, max_sel;
+  float* out;
+  uint32_t* flags;  // [1 + R * H * 4][32] counters and state words, zero between calls
+  uint32_t* stats;  // [R][H][W][4] per-slice key statistics
+  uint32_t* keys;   // [R][H][key_stride]
+  uint32_t* unc;    // [R][H][max_sel] selected blocks decided by the exact selection only
+  float* part_o;    // [R][H][W][G][D]
+  float* part_ml;   // [R][H][W][G][2]
+  int32_t R, H, G, D, dtype, max_blocks, num_pool_blocks, mode, key_stride, max_sel;
   int32_t budget_num, budget_den, min_blocks, local_blocks;
-  int32_t key_stride;
+  float scale_log2;
+  int32_t unroll, nslices, grid;  // from step_geometry / the launcher
 };
-hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+// Slices of the step: passes per slice (unroll) and slices per (request,
+// KV head) (nslices) for these sizes.
+void step_geometry(int dtype, int D, int R, int H, int max_blocks, int* unroll, int* nslices);
+// Bytes of each workspace part of the step, in the order of StepArgs.
+void step_workspace_parts(int dtype, int D, int R, int H, int G, int max_blocks, int max_sel, size_t parts[6]);
+hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
   const void* q;

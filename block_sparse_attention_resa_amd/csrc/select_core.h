@@ -1,0 +1,694 @@
+// Top-n block selection over order-preserving 32-bit score keys, run by one
+// 1024-thread workgroup per (request, KV head), and the device-scope
+// exchange helpers of the kernels that hand keys from workgroup to
+// workgroup inside one launch.
+//
+// "Rectified Sparse Attention" analysis page (paper-graph-ui), §3.4.1 Eq 5
+// (the n - n_local highest-scoring older blocks; ties here go to the lower
+// block id).
+//
+// Thread t owns the consecutive candidate blocks [k t, k t + k) (16-byte
+// loads, kept in registers; rows longer than 32768 blocks fall back to blocks
+// t, t + 1024, ... re-read from memory).  The k-th largest key is found by
+// histogram passes in LDS over monotone bin maps: the first pass bins the
+// candidates' range into 4096 equal-width bins, later passes (rarely needed)
+// bin the key offsets inside the boundary bucket.  Once the boundary bucket
+// holds at most 256 keys they are packed into LDS and ranked, sixteen lanes
+// per member.  Blocks above the threshold are taken, blocks equal to it
+// lowest index first, and one scan of the per-thread counts places every
+// selected id in ascending order.  Wave-wide scans and reductions use DPP
+// lane shifts, and wavefronts whose keys are all candidates run every
+// per-key loop without masks.
+#pragma once
+
+#include "resa_internal.h"
+
+namespace resa {
+
+// ------------------------------------------------- device-scope exchange
+//
+// Data handed between workgroups of one launch is written with device-scope
+// stores (cache policy sc1: written through to the device coherence point),
+// the writer waits for their completion before it signals with an atomic,
+// and the reader, after seeing the signal, reads with device-scope loads, so
+// no write-back or invalidation of whole caches is needed.
+
+__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+// Word quadruple `quad` of a row of `nwords` 32-bit words, read with a
+// 16-byte buffer load at device scope (cache policy sc1).  The row base is
+// uniform over the workgroup; reads past the row return zero.
+__device__ __forceinline__ uint4 load16_agent(const uint32_t* row, int nwords, int quad) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(row), (short)0, nwords * 4, 0x00020000);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, quad * 16, 0, 16);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// Wait until every vector memory access this lane issued has completed
+// (stores and atomics included): vmcnt(0), other counters unconstrained.
+__device__ __forceinline__ void wait_vm_all() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  asm volatile("" ::: "memory");
+}
+
+
+constexpr int kDigitBits = 12;  // histogram pass: 4096 bins
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kFinishMax = 256;  // boundary bucket size the ranking finish takes
+constexpr int kRankLanes = 16;   // lanes (one DPP row) that rank one bucket member
+
+// Cross-lane steps through DPP (row shifts within 16-lane rows, then the
+// row-15 / row-31 broadcasts), which stay in the vector ALU instead of the
+// LDS crossbar.  Lanes that have no source receive `id`.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t id, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  uint32_t v = (uint32_t)x;
+  v += dpp_u32<0x111>(0u, v);  // row_shr:1
+  v += dpp_u32<0x112>(0u, v);  // row_shr:2
+  v += dpp_u32<0x114>(0u, v);  // row_shr:4
+  v += dpp_u32<0x118>(0u, v);  // row_shr:8
+  v += dpp_u32<0x142, 0xa>(0u, v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_u32<0x143, 0xc>(0u, v);  // row_bcast:31 into rows 2 and 3
+  return (int)v;
+}
+
+// Minimum and maximum over the 64 lanes, returned in every lane.
+__device__ __forceinline__ void wave_min_max(uint32_t& mn, uint32_t& mx) {
+  mn = min(mn, dpp_u32<0x111>(0xffffffffu, mn));
+  mx = max(mx, dpp_u32<0x111>(0u, mx));
+  mn = min(mn, dpp_u32<0x112>(0xffffffffu, mn));
+  mx = max(mx, dpp_u32<0x112>(0u, mx));
+  mn = min(mn, dpp_u32<0x114>(0xffffffffu, mn));
+  mx = max(mx, dpp_u32<0x114>(0u, mx));
+  mn = min(mn, dpp_u32<0x118>(0xffffffffu, mn));
+  mx = max(mx, dpp_u32<0x118>(0u, mx));
+  mn = min(mn, dpp_u32<0x142, 0xa>(0xffffffffu, mn));
+  mx = max(mx, dpp_u32<0x142, 0xa>(0u, mx));
+  mn = min(mn, dpp_u32<0x143, 0xc>(0xffffffffu, mn));
+  mx = max(mx, dpp_u32<0x143, 0xc>(0u, mx));
+  mn = (uint32_t)__builtin_amdgcn_readlane((int)mn, 63);
+  mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
+}
+
+// Cross-wavefront exchange slots, two sets used alternately: a call writes
+// its set, waits at one barrier and reads it; the next call of the same kind
+// writes the other set, and the call after that can rewrite the first only
+// after every thread has passed the intervening call's barrier, i.e. after
+// every read of the first call.  So one barrier per call suffices.
+template <typename V, int NW>
+struct WaveSlots {
+  V v[2][NW];
+};
+
+// Exclusive prefix sum over the workgroup in thread order; `total` gets the sum.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, WaveSlots<int, NT / 64>& slots, int& use, int& total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int* lds_waves = slots.v[use];
+  use ^= 1;
+  const int incl = wave_incl_sum(v);
+  if (lane == 63) lds_waves[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int x = lds_waves[w];
+    before += w < wave ? x : 0;
+    total += x;
+  }
+  return before + incl - v;
+}
+
+template <int NT>
+__device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, WaveSlots<uint2, NT / 64>& slots,
+                                              int& use) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint2* lds_mm = slots.v[use];
+  use ^= 1;
+  wave_min_max(mn, mx);
+  if (lane == 0) lds_mm[wave] = make_uint2(mn, mx);
+  __syncthreads();
+  mn = 0xffffffffu;
+  mx = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint2 x = lds_mm[w];
+    mn = min(mn, x.x);
+    mx = max(mx, x.y);
+  }
+}
+
+// Candidate keys of one (request, KV head).  KPT > 0: thread t owns the KPT
+// consecutive blocks [KPT t, KPT t + KPT), read with 16-byte loads before the
+// request's length is known (the row is padded to a multiple of 4 entries and
+// indices are clamped into it), so that a per-thread count and one scan give
+// every selected block its place in the ascending output.  KPT == 0 (any
+// size): thread t owns blocks t + NT j and re-reads the row.
+template <int NT, int KPT>
+struct KeyRuns {
+  static_assert(KPT % 4 == 0, "keys are read four at a time");
+  static_assert(KPT <= 32, "the member mask holds one bit per key");
+  uint32_t reg[KPT > 0 ? KPT : 1];
+  const uint32_t* row;
+  int C, rounds;
+  uint32_t in_mask;  // KPT > 0: bit j set when this thread's key j is a candidate
+  bool full;         // KPT > 0, uniform over the wavefront: every key of every lane is a candidate
+  bool any;          // KPT > 0, uniform over the wavefront: some lane holds a candidate
+  // The keys were written by other workgroups of the same launch: they are
+  // read at device scope (16-byte buffer loads with the device-scope cache
+  // policy), never from a line an earlier read left in a nearer cache.
+  __device__ void prefetch(const uint32_t* kr, int row_stride) {
+    row = kr;
+    if constexpr (KPT > 0) {
+      const int last = row_stride / 4 - 1;
+#pragma unroll
+      for (int v = 0; v < KPT / 4; ++v) {
+        const int idx = (int)threadIdx.x * (KPT / 4) + v;
+        const uint4 x = load16_agent(kr, row_stride, idx < last ? idx : last);
+        reg[4 * v] = x.x;
+        reg[4 * v + 1] = x.y;
+        reg[4 * v + 2] = x.z;
+        reg[4 * v + 3] = x.w;
+      }
+    }
+  }
+  // KPT > 0: keys [KPT t, KPT t + KPT) of an LDS array of at least NT * KPT
+  // entries (entries past the count are ignored).
+  __device__ void load_lds(const uint32_t* keys) {
+    static_assert(KPT > 0, "register-held keys only");
+    row = keys;
+#pragma unroll
+    for (int v = 0; v < KPT / 4; ++v) {
+      const uint4 x = *reinterpret_cast<const uint4*>(keys + ((int)threadIdx.x * (KPT / 4) + v) * 4);
+      reg[4 * v] = x.x;
+      reg[4 * v + 1] = x.y;
+      reg[4 * v + 2] = x.z;
+      reg[4 * v + 3] = x.w;
+    }
+  }
+  __device__ void set_count(int c) {
+    C = c;
+    rounds = (c + NT - 1) / NT;
+    if constexpr (KPT > 0) {
+      const int mine = min(max(c - (int)threadIdx.x * KPT, 0), KPT);  // candidates among this thread's keys
+      in_mask = mine >= 32 ? ~0u : (1u << mine) - 1u;
+      full = __all(mine == KPT) != 0;
+      any = __any(mine > 0) != 0;
+    } else {
+      full = false;
+      any = true;
+    }
+  }
+  __device__ bool valid(int j) const {
+    if constexpr (KPT > 0) return (in_mask >> j) & 1u;
+    else return j < rounds && (int)threadIdx.x + j * NT < C;
+  }
+  __device__ uint32_t key(int j) const {
+    if constexpr (KPT > 0) return reg[j];
+    else return load_agent(row + threadIdx.x + j * NT);
+  }
+  __device__ int nrounds() const { return KPT > 0 ? KPT : rounds; }
+};
+
+// Runs the statements in the variadic argument for every round j of `kr`,
+// with `in` telling whether the lane's key of that round is a candidate.  In
+// wavefronts whose keys are all candidates (all but the last one or two of a
+// row) `in` is the constant true, so those run the statements unmasked;
+// wavefronts without a candidate skip them (every use is a no-op for a key
+// that is not a candidate).  Expects NT, KPT and a KeyRuns `kr` in scope.
+#define RESA_FOR_KEYS(...)                                                       \
+  do {                                                                           \
+    if constexpr (KPT > 0) {                                                     \
+      if (kr.full) {                                                             \
+        _Pragma("unroll") for (int j = 0; j < KPT; ++j) {                        \
+          constexpr bool in = true;                                              \
+          __VA_ARGS__                                                            \
+        }                                                                        \
+      } else if (kr.any) {                                                       \
+        /* opaque copy: the per-key conditions are not kept across phases */    \
+        uint32_t im_ = kr.in_mask;                                               \
+        asm volatile("" : "+v"(im_));                                            \
+        _Pragma("unroll") for (int j = 0; j < KPT; ++j) {                        \
+          const bool in = (im_ >> j) & 1u;                                       \
+          __VA_ARGS__                                                            \
+        }                                                                        \
+      }                                                                          \
+    } else {                                                                     \
+      for (int j = 0; j < kr.rounds; ++j) {                                      \
+        const bool in = (int)threadIdx.x + j * NT < kr.C;                        \
+        __VA_ARGS__                                                              \
+      }                                                                          \
+    }                                                                            \
+  } while (0)
+
+// Monotone map of a key onto kBins histogram bins, built for a bucket whose
+// keys lie in [lo, hi] (keys outside are clamped to the end bins).  By value:
+// bins of equal width in score, which spreads any finite score distribution
+// evenly.  By key: the key offset shifted right, which always separates lo
+// from hi and shrinks the range 2^11-fold per pass; over a range inside one
+// sign and at most two binades it is within 2x of equal width in score and
+// costs fewer instructions, so the first pass uses it there.
+struct BinMap {
+  bool by_value;
+  float fmin, scale;
+  uint32_t lo, hi;
+  int shift;
+  __device__ void init(uint32_t lo_key, uint32_t hi_key, bool allow_value) {
+    lo = lo_key;
+    hi = hi_key;
+    const uint32_t d = hi_key - lo_key;
+    const int nb = d ? 32 - __clz(d) : 0;
+    shift = nb > kDigitBits ? nb - kDigitBits : 0;
+    by_value = false;
+    fmin = 0.f;
+    scale = 0.f;
+    // same sign and exponents at most one apart: key order is near-linear in score
+    const bool narrow = ((lo_key ^ hi_key) >> 31) == 0u && ((hi_key >> 23) - (lo_key >> 23)) <= 1u;
+    if (allow_value && !narrow) {
+      const float a = __uint_as_float(u32_from_order_key(lo_key));
+      const float b = __uint_as_float(u32_from_order_key(hi_key));
+      const float range = b - a;
+      const float s = (float)kBins / range;
+      // lo lands in bin 0; hi must land in bin >= 1 so every pass makes progress
+      if (__builtin_isfinite(a) && __builtin_isfinite(b) && __builtin_isfinite(range) && range > 0.f &&
+          __builtin_isfinite(s) && range * s >= 1.f) {
+        by_value = true;
+        fmin = a;
+        scale = s;
+      }
+    }
+  }
+  __device__ int value_bin(uint32_t key) const {
+    const float f = __uint_as_float(u32_from_order_key(min(max(key, lo), hi)));
+    const int b = (int)((f - fmin) * scale);
+    return min(max(b, 0), kBins - 1);
+  }
+  __device__ int key_bin(uint32_t key) const { return (int)((min(max(key, lo), hi) - lo) >> shift); }
+  // The same maps for a key known to lie in [lo, hi] (no clamping on that
+  // side); any other key gives an unspecified bin.
+  __device__ int value_bin_in(uint32_t key) const {
+    const int b = (int)((__uint_as_float(u32_from_order_key(key)) - fmin) * scale);
+    return min(b, kBins - 1);
+  }
+  __device__ int key_bin_in(uint32_t key) const { return (int)((key - lo) >> shift); }
+  __device__ int operator()(uint32_t key) const { return by_value ? value_bin(key) : key_bin(key); }
+};
+
+// Candidates still in play: keys in [lo, hi] and, after a pass whose range was
+// not re-measured, in histogram bin `bin` of `map`.
+struct Bucket {
+  uint32_t lo, hi;
+  BinMap map;
+  int bin;  // -1: no bin condition
+  __device__ bool has(uint32_t x) const { return x >= lo && x <= hi && (bin < 0 || map(x) == bin); }
+};
+
+// Sum of an int over the sixteen lanes of a DPP row, in every lane of the row.
+__device__ __forceinline__ int row16_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false);  // row_ror:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x124, 0xf, 0xf, false);  // row_ror:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x122, 0xf, 0xf, false);  // row_ror:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x121, 0xf, 0xf, false);  // row_ror:1
+  return x;
+}
+
+// LDS of the selection by an NT-thread workgroup.
+template <int NT>
+struct SelectLds {
+  uint32_t hist2[2][kBins + 1];  // alternating pass histograms; the last slot takes non-members
+  WaveSlots<int, NT / 64> scan_slots;
+  WaveSlots<uint2, NT / 64> mm_slots;
+  uint32_t bucket[kFinishMax];
+  int bc2[2][3];  // boundary record of a pass (bin, rank left, keys), by pass parity
+  int packed;     // keys of the boundary bucket packed so far
+};
+
+// Top-k of the C candidate keys of one row (k in (0, C)) held by `kr`
+// (prefetched, count set), whose range [mn, mx] is known: writes the k
+// selected block ids, ascending, to out.  With unc_out (uniform) it also
+// writes, ascending, the selected ids whose key is at most t_hi and returns
+// their number (0 without unc_out).  Expects the two histograms and
+// `packed` cleared and published by a barrier.  Every thread of the
+// workgroup calls it.
+template <int NT, int KPT>
+__device__ __forceinline__ int select_top(SelectLds<NT>& sl, KeyRuns<NT, KPT>& kr, int C, int k, uint32_t mn,
+                                          uint32_t mx, int32_t* __restrict__ out, uint32_t t_hi = 0u,
+                                          uint32_t* __restrict__ unc_out = nullptr) {
+  constexpr int BPT = kBins / NT;                   // histogram bins per thread in the scan (4 or 8)
+  constexpr bool kKeepBins = KPT > 0 && KPT * NT <= 16 * 1024;  // first-pass bins kept in registers (16 bits each)
+  static_assert(BPT == 4 || BPT == 8, "the scan reads four or eight bins per thread");
+  int scan_use = 0, mm_use = 0;  // alternating slot sets, identical in every thread
+  const int tid = threadIdx.x;
+  const int R = kr.nrounds();
+
+  Bucket bk;
+  bk.lo = mn;
+  bk.hi = mx;
+  bk.bin = -1;
+  bk.map.init(mn, mx, false);
+  int remaining = k;  // keys still to take from the bucket
+  int bucket_n = C;   // keys in the bucket
+  uint32_t bins[kKeepBins ? KPT / 2 : 1];  // first-pass bin of every key, two per register
+#pragma unroll
+  for (int v = 0; v < (kKeepBins ? KPT / 2 : 1); ++v) bins[v] = (uint32_t)kBins | ((uint32_t)kBins << 16);
+
+  // Histogram passes until the bucket holding the k-th largest key is small.
+  int npass = 0;
+  while (bucket_n > kFinishMax && remaining < bucket_n && bk.lo != bk.hi) {
+    if (bk.bin >= 0) {  // re-measure the range of the previous pass's bucket
+      uint32_t a = 0xffffffffu, b = 0u;
+      RESA_FOR_KEYS({
+        const uint32_t x = kr.key(j);
+        const bool m = in && bk.has(x);
+        a = m ? min(a, x) : a;
+        b = m ? max(b, x) : b;
+      });
+      block_min_max<NT>(a, b, sl.mm_slots, mm_use);
+      bk.lo = a;
+      bk.hi = b;
+      bk.bin = -1;
+      if (a == b) break;
+    }
+    BinMap map;
+    map.init(bk.lo, bk.hi, npass == 0);
+    uint32_t* hist = sl.hist2[npass & 1];
+    if (npass == 0) {  // every candidate is in the bucket
+#define RESA_COUNT_KEY(BIN)                                         \
+  {                                                                 \
+    const int b = BIN;                                              \
+    if (in) atomicAdd(&hist[b], 1u); /* constant in full waves */   \
+    if constexpr (kKeepBins) {                                      \
+      const uint32_t kept = in ? (uint32_t)b : (uint32_t)kBins;     \
+      if (j & 1) bins[j / 2] |= kept << 16;                         \
+      else bins[j / 2] = kept;                                      \
+    }                                                               \
+  }
+      // every candidate lies in [min, max] of the candidates
+      if (map.by_value) RESA_FOR_KEYS(RESA_COUNT_KEY(map.value_bin_in(kr.key(j))));
+      else RESA_FOR_KEYS(RESA_COUNT_KEY(map.key_bin_in(kr.key(j))));
+#undef RESA_COUNT_KEY
+    } else {
+      RESA_FOR_KEYS({
+        const uint32_t x = kr.key(j);
+        if (in && bk.has(x)) atomicAdd(&hist[map(x)], 1u);
+      });
+    }
+    __syncthreads();
+    // Suffix counts: thread t owns bins [BPT*rt, BPT*rt + BPT) with rt = NT-1-t,
+    // so an exclusive scan in thread order counts the keys in higher bins.
+    const int rt = NT - 1 - tid;
+    uint32_t hb[BPT];
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; e += 4) {
+      const uint4 h4 = *reinterpret_cast<const uint4*>(&hist[BPT * rt + e]);
+      hb[e] = h4.x;
+      hb[e + 1] = h4.y;
+      hb[e + 2] = h4.z;
+      hb[e + 3] = h4.w;
+      c += (int)(h4.x + h4.y + h4.z + h4.w);
+    }
+    int tot;
+    const int above0 = block_exclusive_scan<NT>(c, sl.scan_slots, scan_use, tot);
+    int* bc = sl.bc2[npass & 1];
+    // this pass's histogram is read; clear it for the pass after next
+#pragma unroll
+    for (int e = 0; e < BPT; e += 4) *reinterpret_cast<uint4*>(&hist[BPT * rt + e]) = make_uint4(0u, 0u, 0u, 0u);
+    if (tid == 0) hist[kBins] = 0u;
+    if (above0 < remaining && above0 + c >= remaining) {
+      int above = above0;
+#pragma unroll
+      for (int e = BPT - 1; e >= 0; --e) {
+        if (above < remaining && above + (int)hb[e] >= remaining) {
+          bc[0] = BPT * rt + e;
+          bc[1] = remaining - above;
+          bc[2] = (int)hb[e];
+        }
+        above += (int)hb[e];
+      }
+    }
+    __syncthreads();
+    bk.map = map;
+    bk.bin = bc[0];
+    remaining = bc[1];
+    bucket_n = bc[2];
+    ++npass;  // the next pass writes the other record, so no barrier is needed here
+  }
+
+  // The threshold: the remaining-th largest key of the bucket.  Keys above it
+  // are taken; of the n_eq keys equal to it, the `take_eq` lowest block ids.
+  uint32_t thr;
+  int take_eq, n_eq;
+  if (bk.lo == bk.hi) {  // every key in the bucket is equal
+    thr = bk.lo;
+    take_eq = remaining;
+    n_eq = bucket_n;
+  } else if (bucket_n <= kFinishMax) {
+    // Ranking finish: the bucket's keys are packed into LDS (slots handed out
+    // by an LDS counter: their order does not matter), then sixteen lanes
+    // rank each member against a sixteenth of the others each; the member
+    // whose rank range holds `remaining` is the threshold.
+    bool kept = false;
+    if constexpr (kKeepBins) kept = npass == 1;
+    if constexpr (KPT > 0) {
+      // members as a bit mask (after one pass, from the kept bins, where
+      // non-candidates hold kBins, which is no bucket's bin); the few lanes
+      // that hold members claim slots one by one
+      uint32_t mem = 0;
+      if (kept) {
+        const uint32_t b2 = (uint32_t)bk.bin | ((uint32_t)bk.bin << 16);
+#pragma unroll
+        for (int j = 0; j < KPT; j += 2) {
+          const uint32_t x = bins[j / 2] ^ b2;
+          mem |= ((x & 0xffffu) == 0u ? 1u : 0u) << j;
+          mem |= ((x >> 16) == 0u ? 2u : 0u) << j;
+        }
+      } else {
+        RESA_FOR_KEYS({ mem |= (in && bk.has(kr.key(j)) ? 1u : 0u) << j; });
+      }
+      if (mem != 0u) {
+        int pos = atomicAdd(&sl.packed, __popc(mem));
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          if ((mem >> j) & 1u) {
+            if (pos < kFinishMax) sl.bucket[pos] = kr.key(j);
+            ++pos;
+          }
+        }
+      }
+    } else {
+      RESA_FOR_KEYS({
+        if (in && bk.has(kr.key(j))) {
+          const int pos = atomicAdd(&sl.packed, 1);
+          if (pos < kFinishMax) sl.bucket[pos] = kr.key(j);
+        }
+      });
+    }
+    __syncthreads();
+    const int nb = bucket_n;  // the members counted by the last pass
+    int* bc = sl.bc2[npass & 1];  // the record the last pass did not use
+    const int sub = tid % kRankLanes;
+    for (int m0 = 0; m0 < nb; m0 += NT / kRankLanes) {  // uniform: every lane of a DPP row takes part
+      const int m = m0 + tid / kRankLanes;
+      const uint32_t x = sl.bucket[m < nb ? m : 0];
+      int gt = 0, eq = 0;
+      for (int qq = sub; qq < nb; qq += kRankLanes) {
+        const uint32_t y = sl.bucket[qq];
+        gt += y > x ? 1 : 0;
+        eq += y == x ? 1 : 0;
+      }
+      gt = row16_sum(gt);
+      eq = row16_sum(eq);
+      if (sub == 0 && m < nb && gt < remaining && remaining <= gt + eq) {  // every writer stores the same values
+        bc[0] = (int)x;
+        bc[1] = remaining - gt;
+        bc[2] = eq;
+      }
+    }
+    __syncthreads();
+    thr = (uint32_t)bc[0];
+    take_eq = bc[1];
+    n_eq = bc[2];
+  } else {
+    // remaining == bucket_n: the whole bucket is taken; the threshold is its
+    // smallest key and every key equal to it lies in the bucket.
+    uint32_t a = 0xffffffffu, b = 0u;
+    RESA_FOR_KEYS({
+      const uint32_t x = kr.key(j);
+      a = (in && bk.has(x)) ? min(a, x) : a;
+    });
+    block_min_max<NT>(a, b, sl.mm_slots, mm_use);
+    thr = a;
+    take_eq = bucket_n;
+    n_eq = bucket_n;
+  }
+
+  // Output in ascending block order.  Each thread's keys are consecutive
+  // blocks, so one scan of the per-thread counts gives every thread its first
+  // output position; ties at the threshold are ranked the same way.
+  const bool ties = take_eq < n_eq;
+  if constexpr (KPT > 0) {
+    uint32_t take = 0;
+    if (!ties) {  // every key at or above the threshold
+      RESA_FOR_KEYS({ take |= (in && kr.key(j) >= thr ? 1u : 0u) << j; });
+    } else {  // of the keys equal to the threshold, the take_eq lowest block ids
+      uint32_t equal = 0;
+      RESA_FOR_KEYS({
+        const uint32_t x = kr.key(j);
+        take |= (in && x > thr ? 1u : 0u) << j;
+        equal |= (in && x == thr ? 1u : 0u) << j;
+      });
+      int n_all;
+      int room = take_eq - block_exclusive_scan<NT>(__popc(equal), sl.scan_slots, scan_use, n_all);
+      for (uint32_t m = equal; m != 0u && room > 0; m &= m - 1u, --room) take |= m & (~m + 1u);
+    }
+    int tot;
+    int pos = block_exclusive_scan<NT>(__popc(take), sl.scan_slots, scan_use, tot);
+    const int first = tid * KPT;
+    for (uint32_t m = take; m != 0u; m &= m - 1u, ++pos)
+      if (pos < k) out[pos] = first + __builtin_ctz(m);
+    int n_unc = 0;
+    if (unc_out) {
+      uint32_t above = 0;
+      RESA_FOR_KEYS({ above |= (in && kr.key(j) > t_hi ? 1u : 0u) << j; });
+      const uint32_t unc = take & ~above;
+      int upos = block_exclusive_scan<NT>(__popc(unc), sl.scan_slots, scan_use, n_unc);
+      for (uint32_t m = unc; m != 0u; m &= m - 1u, ++upos)
+        if (upos < k) store_agent(unc_out + upos, (uint32_t)(first + __builtin_ctz(m)));
+    }
+    return n_unc;
+  } else {
+    // Any number of rounds: one block scan per round.
+    int base_out = 0, base_eq = 0, base_unc = 0;
+    for (int j = 0; j < R; ++j) {
+      const bool v = kr.valid(j);
+      const uint32_t x = kr.key(j);
+      const bool is_eq = v && x == thr;
+      int tot_eq;
+      const int eq_before = block_exclusive_scan<NT>(is_eq ? 1 : 0, sl.scan_slots, scan_use, tot_eq);
+      const bool t = (v && x > thr) || (is_eq && (!ties || base_eq + eq_before < take_eq));
+      int tot;
+      const int pos = block_exclusive_scan<NT>(t ? 1 : 0, sl.scan_slots, scan_use, tot);
+      if (t && base_out + pos < k) out[base_out + pos] = tid + j * NT;
+      if (unc_out) {
+        const bool u = t && x <= t_hi;
+        int tot_u;
+        const int upos = block_exclusive_scan<NT>(u ? 1 : 0, sl.scan_slots, scan_use, tot_u);
+        if (u && base_unc + upos < k) store_agent(unc_out + base_unc + upos, (uint32_t)(tid + j * NT));
+        base_unc += tot_u;
+      }
+      base_out += tot;
+      base_eq += tot_eq;
+    }
+    return base_unc;
+  }
+}
+
+// ------------------------------------------------------------ band select
+//
+// The top-k with a known bracket of the threshold: given lo <= thr <= hi,
+// where thr is the k-th largest candidate key and fewer than k keys exceed
+// hi, every key above hi is taken, no key below lo is, and only the keys in
+// [lo, hi] (the band) need ranking.  The band is packed into LDS in
+// ascending block order (so a lower slot is a lower block id) and the
+// (k - #above)-th largest of it is found by select_top on the packed keys.
+
+constexpr int kBandMax = 4096;  // band keys the LDS holds
+
+struct BandLds {
+  __align__(16) uint32_t key[kBandMax];  // band keys, ascending block order
+  int id[kBandMax];                       // their block ids
+  int slot[kBandMax];                     // selected band slots, ascending
+  uint32_t taken[kBandMax / 32];          // bit per band slot
+};
+
+// Writes the k selected block ids of the C candidates held by `kr`
+// (prefetched, count set; KPT > 0), ascending, to out, and the selected ids
+// whose key is at most hi, ascending, to unc_out (device-scope stores);
+// returns their number.  Returns -1, having written nothing, when the band
+// holds more than kBandMax keys.  Expects the two histograms and `packed` of
+// `sl` cleared and published by a barrier.  Every thread calls it.
+template <int NT, int KPT>
+__device__ __forceinline__ int select_band(SelectLds<NT>& sl, BandLds& bl, KeyRuns<NT, KPT>& kr, int k,
+                                           uint32_t lo, uint32_t hi, int32_t* __restrict__ out,
+                                           uint32_t* __restrict__ unc_out) {
+  static_assert(KPT > 0 && NT * KPT <= 16384, "register-held keys; counts fit in 16 bits");
+  constexpr int KPB = kBandMax / NT;  // band keys per thread in the band selection
+  static_assert(KPB % 4 == 0 && KPB <= 32, "band keys are read four at a time");
+  int scan_use = 0;
+  const int tid = threadIdx.x;
+  const int first = tid * KPT;
+  uint32_t above = 0, band = 0;
+  RESA_FOR_KEYS({
+    const uint32_t x = kr.key(j);
+    above |= (in && x > hi ? 1u : 0u) << j;
+    band |= (in && x >= lo && x <= hi ? 1u : 0u) << j;
+  });
+  for (int q = tid; q < kBandMax / 32; q += NT) bl.taken[q] = 0u;
+  int tot;
+  const int pre = block_exclusive_scan<NT>((__popc(band) << 16) | __popc(above), sl.scan_slots, scan_use, tot);
+  const int nb = tot >> 16;
+  const int k2 = k - (tot & 0xffff);  // keys to take from the band: 1 <= k2 <= nb
+  if (nb > kBandMax || k2 < 1 || k2 > nb) return -1;  // uniform
+  const int p0 = pre >> 16;  // this thread's first band slot
+  {
+    int pos = p0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if ((band >> j) & 1u) {
+        bl.key[pos] = kr.key(j);
+        bl.id[pos] = first + j;
+        ++pos;
+      }
+    }
+  }
+  __syncthreads();
+  if (k2 == nb) {
+    for (int q = tid; q < nb; q += NT) bl.slot[q] = q;
+  } else {
+    KeyRuns<NT, KPB> kb;
+    kb.load_lds(bl.key);
+    kb.set_count(nb);
+    select_top<NT, KPB>(sl, kb, nb, k2, lo, hi, bl.slot);
+  }
+  __syncthreads();
+  for (int q = tid; q < k2; q += NT) {
+    const int sl_q = bl.slot[q];
+    atomicOr(&bl.taken[sl_q >> 5], 1u << (sl_q & 31));
+    store_agent(unc_out + q, (uint32_t)bl.id[sl_q]);
+  }
+  __syncthreads();
+  uint32_t take = above;
+  {
+    int pos = p0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if ((band >> j) & 1u) {
+        take |= ((bl.taken[pos >> 5] >> (pos & 31)) & 1u) << j;
+        ++pos;
+      }
+    }
+  }
+  int n_all;
+  int pos = block_exclusive_scan<NT>(__popc(take), sl.scan_slots, scan_use, n_all);
+  for (uint32_t m = take; m != 0u; m &= m - 1u, ++pos)
+    if (pos < k) out[pos] = first + __builtin_ctz(m);
+  return k2;
+}
+
+}  // namespace resa

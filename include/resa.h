@@ -15,6 +15,8 @@
  *   resa_dense_rectify      dense rectification (§3.4.2): write the last f
  *                           positions' rows, refresh their descriptors, and
  *                           run causal chunk attention over the whole cache
+ *   resa_sparse_step        resa_score_select followed by resa_sparse_decode
+ *                           as one launch (the decode step of one layer)
  *
  * Conventions for every call
  * --------------------------
@@ -89,7 +91,8 @@ typedef enum {
   RESA_OP_SCORE_SELECT = 1,
   RESA_OP_SPARSE_DECODE = 2,
   RESA_OP_DENSE_DECODE = 3,
-  RESA_OP_DENSE_RECTIFY = 4
+  RESA_OP_DENSE_RECTIFY = 4,
+  RESA_OP_SPARSE_STEP = 5
 } resa_op;
 
 /* Method configuration, passed by pointer to every call. */
@@ -136,8 +139,12 @@ int32_t resa_selection_count(const resa_config* cfg, int32_t num_blocks);
 /* Bytes of workspace `op` needs for `num_requests` requests of up to
  * `max_blocks` blocks; `max_sel` is the sel_idx row capacity (sparse ops) and
  * `chunk` the rectification window (rectify).  Returns 0 on invalid arguments.
- * Workspace contents need no initialisation; calls that share a workspace
- * must be ordered on one stream. */
+ * Calls that share a workspace must be ordered on one stream.
+ * Initialisation: the workspaces of RESA_OP_SCORE_SELECT and
+ * RESA_OP_SPARSE_STEP hold counters that workgroups of one launch use to hand
+ * work to each other; they must be all zero when the workspace is first
+ * used (allocate it zeroed), and every call leaves them zero again.  The
+ * other workspaces need no initialisation. */
 size_t resa_workspace_bytes(const resa_config* cfg, int32_t op, int32_t num_requests,
                             int32_t max_blocks, int32_t max_sel, int32_t chunk);
 
@@ -205,6 +212,30 @@ resa_status resa_sparse_decode(const resa_config* cfg, const resa_paged_kv* kv,
                                int32_t num_requests, const void* q, const int32_t* sel_idx,
                                const int32_t* sel_cnt, int32_t max_sel, float* out, void* ws,
                                size_t ws_bytes, void* stream);
+
+/*
+ * One decode step of one layer: exactly what resa_score_select(cfg, kv,
+ * num_requests, q, refresh_tail, sel_idx, sel_cnt, max_sel, NULL, ...)
+ * followed by resa_sparse_decode(cfg, kv, num_requests, q, sel_idx, sel_cnt,
+ * max_sel, out, ...) compute - the same sel_idx and sel_cnt, and out within
+ * floating-point rounding of the two-call result (the attention is split
+ * differently) - in a single persistent launch.  Blocks whose score already
+ * proves them selected (a bound from per-slice order statistics, see the
+ * kernel source) are attended while the exact selection is still running.
+ * The launch keeps at most one workgroup per compute unit and its
+ * workgroups wait for each other (bounded waits, each about a second at
+ * most); it relies on all of them being resident at once, which holds when
+ * no other work occupies the device's compute units during the call.
+ * Requires max_sel >= resa_selection_count(cfg, kv->max_blocks) and
+ * ws_bytes >= resa_workspace_bytes(cfg, RESA_OP_SPARSE_STEP, num_requests,
+ * kv->max_blocks, max_sel, 0), a workspace whose counters are zero (see
+ * resa_workspace_bytes).  Reads q, k_pool, v_pool, desc_pool, block_table,
+ * seq_lens (and writes the last block's descriptor when refresh_tail != 0);
+ * writes sel_idx, sel_cnt, out [R][H*g][d] float32.
+ */
+resa_status resa_sparse_step(const resa_config* cfg, const resa_paged_kv* kv, int32_t num_requests,
+                             const void* q, int32_t refresh_tail, int32_t* sel_idx, int32_t* sel_cnt,
+                             int32_t max_sel, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * resa_sparse_decode without a caller workspace, for callers that cannot

@@ -101,7 +101,7 @@ def test_workspace_and_splits(lib):
     ("num_kv_heads", 0, 1), ("group_size", 0, 1), ("group_size", 17, 2), ("head_dim", 96, 2),
     ("block_size", 32, 2), ("dtype", 5, 1), ("budget_num", 0, 1), ("budget_num", 11, 1),
     ("budget_den", 0, 1), ("min_blocks", -1, 1), ("local_blocks", 0, 1), ("score_mode", 7, 1),
-    ("sm_scale", 0.0, 1), ("sm_scale", float("nan"), 1), ("num_splits", -2, 1), ("num_kv_heads", 65, 2),
+    ("sm_scale", 0.0, 1), ("sm_scale", float("nan"), 1), ("num_splits", -2, 1), ("num_kv_heads", 65536, 2),
 ])
 def test_bad_config_rejected(lib, field, value, status):
     c = cfg()

@@ -1,0 +1,161 @@
+"""resa_sparse_step (score, select and sparse attention in one persistent
+launch) against the CPU oracle and against the two-call path
+(resa_score_select + resa_sparse_decode): the same selection id for id, the
+tail descriptor refreshed bit-exactly, and attention outputs within the
+output tolerance of the oracle on the selected blocks.  Covers the small
+parity cases (ragged, permuted pools, NaN padding, d = 64, fp32, g = 16,
+mean-pooled scoring, wider local windows, the n_min floor, extra table
+columns), the full-size workloads, repeated calls on one workspace (the
+launch resets its counters) and graph replays."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_resa_amd as resa
+import oracle as O
+from synth import WORKLOADS, num_blocks
+from tests import gpu_common as C
+from tests.test_gpu_parity import CASES, make, oracle_scores
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    C.require_gpu()
+
+
+def run_step(case, q=None, refresh_tail=False, ws=None):
+    R, H, HG, d = case.R, case.spec.num_kv_heads, case.spec.num_q_heads, case.spec.head_dim
+    ms = C.max_sel_for(case)
+    sel_idx = torch.full((R, H, ms), -7, dtype=torch.int32, device="cuda")
+    sel_cnt = torch.full((R, H), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((R, HG, d), float("nan"), device="cuda")
+    if ws is None:
+        ws = resa.alloc_workspace(case.cfg, resa.OP_SPARSE_STEP, R, case.kv.max_blocks, ms)
+    resa.sparse_step(case.cfg, case.kv, case.inp.q if q is None else q, sel_idx, sel_cnt, out, ws,
+                     refresh_tail=refresh_tail)
+    return sel_idx, sel_cnt, out
+
+
+def check_step_against_oracle(case, sel_idx, sel_cnt, out, q=None, tag=""):
+    lists = C.sel_lists(sel_idx, sel_cnt)
+    g = case.spec.group_size
+    scale = C.sm_scale(case.cfg)
+    qq = case.inp.q if q is None else q
+    for r in range(case.R):
+        L = case.inp.seq_lens[r]
+        for i in range(case.spec.num_kv_heads):
+            K, V = C.keys_of(case, r, i), C.values_of(case, r, i)
+            qg = C.np64(qq[r, i * g:(i + 1) * g])
+            lo, hi = O.descriptors(K, L)
+            mode = O.SCORE_MEAN_POOL if case.cfg.score_mode == resa.RESA_SCORE_MEAN_POOL else O.SCORE_SUM_HEADS
+            C.check_selection(O.scores(qg, lo, hi, mode), lists[r][i], case.cfg, tag=f"{tag} r{r} i{i}")
+            C.check_out(out[r, i * g:(i + 1) * g].cpu().numpy(), O.attend(qg, K, V, L, lists[r][i], scale),
+                        f"{tag} step r{r} i{i}")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_step_matches_two_calls_and_oracle(name):
+    case = make(name)
+    C.run_descriptors(case)
+    sel_ref, cnt_ref, _ = C.run_score_select(case, with_scores=False)
+    out_ref = C.run_sparse(case, sel_ref, cnt_ref)
+    sel_idx, sel_cnt, out = run_step(case)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_idx, sel_ref) and torch.equal(sel_cnt, cnt_ref), "selection differs from score_select"
+    C.check_out(out.cpu().numpy(), out_ref.cpu().numpy().astype(np.float64), f"{name} vs two calls")
+    check_step_against_oracle(case, sel_idx, sel_cnt, out, tag=name)
+
+
+@pytest.mark.parametrize("name", ["bf16_d128_L647", "bf16_ragged_r3_perm_nan", "tiny_f32_ctx2k"])
+def test_step_refreshes_tail_descriptor(name):
+    case = make(name)
+    C.run_descriptors(case)
+    full = case.kv.desc_pool.clone()
+    for r, L in enumerate(case.inp.seq_lens):
+        p = int(case.kv.block_table[r, num_blocks(L) - 1])
+        case.kv.desc_pool[p] = 7.0
+    sel_idx, sel_cnt, out = run_step(case, refresh_tail=True)
+    torch.cuda.synchronize()
+    assert torch.equal(C.desc_bits(case.kv.desc_pool), C.desc_bits(full))
+    check_step_against_oracle(case, sel_idx, sel_cnt, out, tag=name)
+
+
+def test_step_repeated_calls_on_one_workspace():
+    """Counters and state words return to zero after each launch: several
+    calls with different queries on one workspace, each checked."""
+    case = make("bf16_extra_table_cols")
+    C.run_descriptors(case)
+    ms = C.max_sel_for(case)
+    ws = resa.alloc_workspace(case.cfg, resa.OP_SPARSE_STEP, case.R, case.kv.max_blocks, ms)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    for rep in range(3):
+        q = torch.randn(case.inp.q.shape, device="cuda", generator=gen).to(case.inp.q.dtype)
+        sel_idx, sel_cnt, out = run_step(case, q=q, ws=ws)
+        torch.cuda.synchronize()
+        check_step_against_oracle(case, sel_idx, sel_cnt, out, q=q, tag=f"rep{rep}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,seed,layer", [("qwen7b_ctx32k_b1", 101, 0), ("qwen7b_ragged_b8", 102, 0),
+                                             ("qwen7b_ctx256k_l28", 2024, 0)])
+def test_step_full_size_workloads(name, seed, layer):
+    spec = WORKLOADS[name]
+    case = C.make_case(spec, seed=seed, layer=layer, permute=name == "qwen7b_ragged_b8")
+    C.run_descriptors(case)
+    sel_idx, sel_cnt, out = run_step(case, refresh_tail=True)
+    sel_ref, cnt_ref, _ = C.run_score_select(case, with_scores=False)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_idx, sel_ref) and torch.equal(sel_cnt, cnt_ref)
+    check_step_against_oracle(case, sel_idx, sel_cnt, out, tag=name)
+
+
+def test_step_graph_replays_match_oracle():
+    """The step of three layers captured in a HIP graph, replayed four times
+    with eager work and synchronisations in between; every replay is checked
+    against the oracle and is bit-identical to the eager call."""
+    spec = WORKLOADS["qwen7b_ctx32k_b1"]
+    cases = [C.make_case(spec, seed=400 + l) for l in range(3)]
+    R, H, g, d = 1, spec.num_kv_heads, spec.group_size, spec.head_dim
+    state = []
+    for case in cases:
+        C.run_descriptors(case)
+        ms = C.max_sel_for(case)
+        state.append(dict(case=case, sel_idx=torch.full((R, H, ms), -5, dtype=torch.int32, device="cuda"),
+                          sel_cnt=torch.zeros((R, H), dtype=torch.int32, device="cuda"),
+                          out=torch.zeros((R, H * g, d), device="cuda"),
+                          ws=resa.alloc_workspace(case.cfg, resa.OP_SPARSE_STEP, R, case.kv.max_blocks, ms)))
+
+    def step():
+        for st in state:
+            c = st["case"]
+            resa.sparse_step(c.cfg, c.kv, c.inp.q, st["sel_idx"], st["sel_cnt"], st["out"], st["ws"],
+                             refresh_tail=True)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [(st["sel_idx"].clone(), st["out"].clone()) for st in state]
+    for st in state:
+        check_step_against_oracle(st["case"], st["sel_idx"], st["sel_cnt"], st["out"], tag="eager")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        for st in state:
+            st["out"].fill_(float("nan"))
+            st["sel_idx"].fill_(-9)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for st, (si, o) in zip(state, eager):
+            assert torch.equal(st["sel_idx"], si), f"replay {rep}: selection differs"
+            assert torch.equal(st["out"], o), f"replay {rep}: output differs"
+            check_step_against_oracle(st["case"], st["sel_idx"], st["sel_cnt"], st["out"], tag=f"replay{rep}")
