@@ -16,9 +16,15 @@ only (the pages measure kernel time without CPU overhead, §5).  Reported:
 * value: microseconds per layer-step (lower is better);
 * achieved HBM GB/s of the layer-step on its algorithmic bytes;
 * the build's own dense decode (resa_dense_decode) at the same shape;
-* the rectification call (window 32) at the same shape;
-* roofline of the dominant kernel (sparse decode) from HIP events;
-* the CPU oracle timed on a bounded sample of the same step.
+* the rectification call (window 32) at the same shape, and at the
+  rectification workload (4 requests x 131072 tokens, window 64);
+* a streaming reference measured in the same run: the runtime's device copy
+  at 54 MiB (the sparse decode's size) and at 1 GiB, timed with HIP events;
+* roofline of the dominant kernel (sparse decode): the event-timed call, the
+  kernel's own duration from the committed kernel trace, the whole step;
+* the CPU oracle timed on bounded samples (a 256K layer-step, a 32K
+  layer-step, one rectification of a 131K KV head), on every core this
+  process may use.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -91,6 +97,121 @@ def measured_traffic(kernel_hash):
     if rec.get("kernel_source_hash") != kernel_hash:
         return None, None
     return rec.get("hbm_bytes_per_launch"), rec.get("rocprof_avg_us")
+
+
+C5_NAME = "qwen7b_ctx131k_b4_rectify"
+C2_NAME = "qwen7b_ctx32k_b1"
+
+
+def oracle_layer_step(O, qs, Ks, Vs, desc, L, scale):
+    """One layer-step of the oracle: per KV head the tail block's descriptor,
+    the block scores, the selection and attention over the selected blocks."""
+    for i in range(len(qs)):
+        lo, hi = desc[i]
+        lo[-1], hi[-1] = O.block_descriptor(Ks[i], L, (L + 15) // 16 - 1)
+        S = O.scores(qs[i], lo, hi)
+        blocks = O.select(S)
+        O.attend(qs[i], Ks[i], Vs[i], L, blocks, scale)
+
+
+def time_reps(fn, budget_s, max_reps):
+    reps = 0
+    t0 = time.perf_counter()
+    while reps < 1 or (time.perf_counter() - t0 < budget_s and reps < max_reps):
+        fn()
+        reps += 1
+    return (time.perf_counter() - t0) / reps, reps
+
+
+def cpu_oracle_legs(O, np, torch, spec4, keep0, scale):
+    """The oracle (fp64 NumPy, as it stands) on the host's cores: the 256K
+    layer-step (the headline unit), a 32K layer-step and the rectification of
+    one 131K KV head at window 64.  The two layer-steps use the workloads'
+    seeded synthetic layers (the 256K one is the GPU run's layer 0); the
+    rectification's cache is seeded N(0, 1) rows of the same shape (the
+    oracle's cost does not depend on the values).  Returns the cpu_baseline
+    record."""
+    from threadpoolctl import threadpool_limits
+
+    from synth import WORKLOADS, make_layer, make_rectify_inputs
+
+    cores = len(os.sched_getaffinity(0))
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    legs = {}
+    with threadpool_limits(limits=cores):
+        # 256K layer-step (layer 0 of the timed stack)
+        q0, k0, v0 = keep0
+        H, g = spec4.num_kv_heads, spec4.group_size
+        L4 = spec4.seq_lens[0]
+        qs = [f64(q0[0, i * g:(i + 1) * g]) for i in range(H)]
+        Ks = [f64(k0[0][i]) for i in range(H)]
+        Vs = [f64(v0[0][i]) for i in range(H)]
+        desc = [O.descriptors(Ks[i], L4) for i in range(H)]  # the cache state before the step (not timed)
+        sec, reps = time_reps(lambda: oracle_layer_step(O, qs, Ks, Vs, desc, L4, scale), 10.0, 5)
+        legs["ctx256k_layer_step_us"] = round(sec * 1e6, 1)
+        legs["ctx256k_reps"] = reps
+        del Ks, Vs, desc
+        # 32K layer-step
+        spec2 = WORKLOADS[C2_NAME]
+        inp = make_layer(spec2, seed=SEED, layer=0)
+        L2 = spec2.seq_lens[0]
+        qs = [f64(inp.q[0, i * g:(i + 1) * g]) for i in range(H)]
+        Ks = [f64(inp.keys[0][i]) for i in range(H)]
+        Vs = [f64(inp.values[0][i]) for i in range(H)]
+        desc = [O.descriptors(Ks[i], L2) for i in range(H)]
+        sec, reps = time_reps(lambda: oracle_layer_step(O, qs, Ks, Vs, desc, L2, scale), 4.0, 20)
+        legs["ctx32k_layer_step_us"] = round(sec * 1e6, 1)
+        legs["ctx32k_reps"] = reps
+        del inp, Ks, Vs, desc
+        # rectification of one KV head of one 131K request at window 64; the
+        # call rectifies 4 requests x 4 KV heads, so the per-call figure is 16x
+        spec5 = WORKLOADS[C5_NAME]
+        f = spec5.rectify_chunk
+        L5 = spec5.seq_lens[0]
+        k5 = torch.Generator().manual_seed(SEED)
+        K5 = np.asarray(torch.randn((L5, spec5.head_dim), generator=k5).to(torch.bfloat16).float().numpy(),
+                        dtype=np.float64)
+        V5 = np.asarray(torch.randn((L5, spec5.head_dim), generator=k5).to(torch.bfloat16).float().numpy(),
+                        dtype=np.float64)
+        qc, kn, vn = make_rectify_inputs(spec5.with_(num_requests=1), 131, f)
+        qh, knh, vnh = f64(qc[0, :, :g]), f64(kn[0, :, 0]), f64(vn[0, :, 0])
+        sec, reps = time_reps(lambda: O.rectify(qh, knh, vnh, K5, V5, L5, scale), 1.0, 1)
+        units = spec5.num_requests * spec5.num_kv_heads
+        legs["rectify_131k_f64_us_per_call"] = round(sec * 1e6 * units, 1)
+        legs["rectify_sample_kv_heads"] = 1
+        del K5, V5
+    return {"value": legs["ctx256k_layer_step_us"], "unit": "us/layer-step", "cores": cores, "kind": "oracle",
+            "sample": (f"256K: {legs['ctx256k_reps']} layer-step(s) of layer 0 (4 KV heads: tail descriptor, "
+                       f"16384 block scores, top-1639 selection, attention over the selected blocks); 32K: "
+                       f"{legs['ctx32k_reps']} layer-step(s); rectification: one KV head of one 131072-token "
+                       f"request at window 64, scaled by the call's 16 (request, KV head) pairs; "
+                       f"NumPy fp64 on {cores} threads"),
+            "legs": legs}
+
+
+def copy_reference(torch, nbytes, reps):
+    """The runtime's device copy (torch copy_) of nbytes, timed with HIP events
+    over back-to-back copies that cycle through enough buffer pairs to touch
+    more than 1 GiB, so no copy reads from the last-level cache.  Returns
+    (us per copy, GB/s counting the bytes read and written)."""
+    n = nbytes // 2
+    nbuf = max(1, min(24, -(-(1 << 30) // nbytes)))
+    src = [torch.ones(n, dtype=torch.bfloat16, device="cuda") for _ in range(nbuf)]
+    dst = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(nbuf)]
+    for j in range(nbuf):
+        dst[j].copy_(src[j])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(reps):
+        dst[k % nbuf].copy_(src[k % nbuf])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return us, 2 * nbytes / (us * 1e-6) / 1e9
 
 
 def main(argv=None):
@@ -267,14 +388,14 @@ def main(argv=None):
     dec_bytes = ab["kv"] + ab["q"] + ab["out"]
     dec_gbps = dec_bytes / (t_dec * 1e-6) / 1e9
     khash = source_hash("decode.hip", "attn_frag.h", "resa_internal.h")
-    traffic, trace_us = measured_traffic(khash)
+    traffic, trace = measured_traffic(khash)
+    trace_us = trace.get("decode") if isinstance(trace, dict) else None
 
     # ---------------------------------------------------------------- check + CPU oracle
     cpu = None
     check = None
     if keep0 is not None:
         import oracle as O
-        from threadpoolctl import threadpool_limits
 
         torch.cuda.synchronize()
         q0, k0, v0 = keep0
@@ -295,25 +416,10 @@ def main(argv=None):
             errs.append(float(np.abs(out0[0, i * g:(i + 1) * g] - ref).max()))
         check = max(errs)
         log(f"layer-0 output vs oracle: max abs err {check:.2e}")
-        log("oracle: timing the layer-step on the host")
-        reps = 0
-        t0 = time.perf_counter()
-        with threadpool_limits(limits=1):
-            while reps < 1 or (time.perf_counter() - t0 < 10.0 and reps < 5):
-                for i in range(H):
-                    lo, hi = desc[i]
-                    lo[-1], hi[-1] = O.block_descriptor(Ks[i], L, (L + 15) // 16 - 1)
-                    S = O.scores(qs[i], lo, hi)
-                    blocks = O.select(S)
-                    O.attend(qs[i], Ks[i], Vs[i], L, blocks, scale)
-                reps += 1
-        cpu_us = (time.perf_counter() - t0) / reps * 1e6
-        cpu = {"value": round(cpu_us, 1), "unit": "us/layer-step", "cores": 1, "kind": "oracle",
-               "sample": f"{reps} layer-step(s) of layer 0 (4 KV heads: tail descriptor, 16384 block "
-                         f"scores, top-1639 selection, attention over the selected blocks), NumPy fp64, "
-                         f"1 thread"}
-        log(f"oracle: {cpu_us / 1e3:.1f} ms per layer-step ({reps} reps)")
         del Ks, Vs, desc
+        log(f"oracle: timing on the host ({len(os.sched_getaffinity(0))} threads)")
+        cpu = cpu_oracle_legs(O, np, torch, spec, keep0, scale)
+        log(f"oracle: {cpu['legs']}")
 
     # ---------------------------------------------------------------- rectification
     qc = torch.randn((1, RECT_CHUNK, H * g, d), device="cuda").to(torch.bfloat16)
@@ -328,6 +434,37 @@ def main(argv=None):
     t_rect = per_call(rectify)  # every replay rewrites the same window
     rect_flops = H * g * sum(4 * d * (L - RECT_CHUNK + t + 1) for t in range(RECT_CHUNK))
     log(f"rectify (window {RECT_CHUNK}): {t_rect:.1f} us/layer, {rect_flops / (t_rect * 1e-6) / 1e12:.1f} TFLOP/s")
+
+    # rectification workload: 4 requests x 131072 tokens, window 64
+    spec5 = WORKLOADS[C5_NAME]
+    f5 = spec5.rectify_chunk
+    inp5 = make_layer(spec5, seed=SEED, layer=0, device="cuda")
+    pg5 = make_paged(inp5)
+    kv5 = resa.PagedKV(pg5.k_pool, pg5.v_pool, pg5.desc_pool, pg5.block_table, pg5.seq_lens)
+    resa.build_descriptors(cfg, kv5)
+    lens5 = list(inp5.seq_lens)
+    del inp5
+    R5 = len(lens5)
+    qc5 = torch.randn((R5, f5, H * g, d), device="cuda").to(torch.bfloat16)
+    kn5 = torch.randn((R5, f5, H, d), device="cuda").to(torch.bfloat16)
+    vn5 = torch.randn((R5, f5, H, d), device="cuda").to(torch.bfloat16)
+    rout5 = torch.empty((R5, f5, H * g, d), device="cuda")
+    ws_r5 = resa.alloc_workspace(cfg, resa.OP_DENSE_RECTIFY, R5, kv5.max_blocks, chunk=f5)
+    gr5 = capture(lambda: resa.dense_rectify(cfg, kv5, qc5, kn5, vn5, rout5, ws_r5))
+    _, ev5 = time_graph(gr5, max(5, args.steps // 5), 2)  # every replay rewrites the same windows
+    del gr5
+    t_rect5 = ev5 * 1e3
+    flops5 = H * g * sum(4 * d * (L5 - f5 + t + 1) for L5 in lens5 for t in range(f5))
+    kv_bytes5 = sum(H * L5 * 2 * d * e for L5 in lens5)
+    log(f"rectify {C5_NAME}: {t_rect5:.1f} us/call, {flops5 / (t_rect5 * 1e-6) / 1e12:.1f} TFLOP/s")
+    del kv5, pg5, qc5, kn5, vn5, rout5, ws_r5
+    torch.cuda.empty_cache()
+
+    # streaming reference in the same run: the runtime's device copy
+    copy54_us, copy54_gbps = copy_reference(torch, 54 << 20, 200)
+    copy1g_us, copy1g_gbps = copy_reference(torch, 1 << 30, 20)
+    log(f"device copy: 54 MiB {copy54_us:.2f} us ({copy54_gbps:.0f} GB/s read+write), "
+        f"1 GiB {copy1g_us:.1f} us ({copy1g_gbps:.0f} GB/s)")
 
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib * 2**20 // 4
@@ -365,11 +502,30 @@ def main(argv=None):
         "rectify_us_per_layer": round(t_rect, 1),
         "rectify_window": RECT_CHUNK,
         "rectify_tflops": round(rect_flops / (t_rect * 1e-6) / 1e12, 2),
-        "roofline": {"bound": "hbm", "kernel": "sparse decode (resa_sparse_decode)",
+        "rectify_c5": {"workload": C5_NAME, "requests": R5, "ctx": lens5[0], "window": f5,
+                       "us_per_call": round(t_rect5, 1),
+                       "useful_tflops": round(flops5 / (t_rect5 * 1e-6) / 1e12, 1),
+                       "frac_of_bf16_mfma_peak": round(flops5 / (t_rect5 * 1e-6) / 2.5e15, 4),
+                       "cache_bytes": kv_bytes5,
+                       "cache_stream_gbps": round(kv_bytes5 / (t_rect5 * 1e-6) / 1e9, 1)},
+        "stream_reference": {"kind": "runtime device copy (torch copy_), HIP events, buffers cycled past the "
+                                     "last-level cache; GB/s counts bytes read + written",
+                             "copy_54MiB_us": round(copy54_us, 2), "copy_54MiB_gbps": round(copy54_gbps, 1),
+                             "copy_1GiB_us": round(copy1g_us, 1), "copy_1GiB_gbps": round(copy1g_gbps, 1)},
+        "roofline": {"bound": "hbm",
+                     "kernel": "sparse decode call (resa_sparse_decode: decode_kernel + merge_kernel)",
                      "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": dec_bytes, "avg_launch_us": round(t_dec, 3),
-                     "trace_avg_us": trace_us, "kernel_source_hash": khash},
+                     "timing": "event-timed call: HIP events around graph replays of the call over 28 layers",
+                     "trace_kernel": "decode_kernel<bf16_t, 128, true, 8>",
+                     "trace_avg_us": trace_us,
+                     "trace_kernel_frac": (round(dec_bytes / (trace_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
+                                           if trace_us else None),
+                     "step_frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "frac_of_copy_54MiB": round(dec_gbps / copy54_gbps, 4),
+                     "step_frac_of_copy_54MiB": round(gbps / copy54_gbps, 4),
+                     "kernel_source_hash": khash},
         "cpu_baseline": cpu,
         "oracle_check_max_abs_err": check,
     }

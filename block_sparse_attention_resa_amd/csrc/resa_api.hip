@@ -129,7 +129,7 @@ size_t workspace_bytes(const resa_config* c, int op, int R, int max_blocks, int 
       return partial_bytes(c, R, S, (long long)chunk * c->group_size);
     }
     case RESA_OP_SPARSE_STEP: {
-      size_t parts[6];
+      size_t parts[kStepParts];
       step_workspace_parts(c->dtype, c->head_dim, R, c->num_kv_heads, c->group_size, max_blocks, max_sel, parts);
       size_t total = 0;
       for (size_t b : parts) total += align_up(b);
@@ -405,22 +405,23 @@ resa_status resa_sparse_step(const resa_config* cfg, const resa_paged_kv* kv, in
   a.sel_idx = sel_idx;
   a.sel_cnt = sel_cnt;
   a.out = out;
-  size_t parts[6];
+  size_t parts[kStepParts];
   step_workspace_parts(cfg->dtype, cfg->head_dim, num_requests, cfg->num_kv_heads, cfg->group_size, kv->max_blocks,
                        max_sel, parts);
   char* base = static_cast<char*>(ws);
   size_t off = 0;
-  void* ptr[6];
-  for (int k = 0; k < 6; ++k) {
+  void* ptr[kStepParts];
+  for (int k = 0; k < kStepParts; ++k) {
     ptr[k] = base + off;
     off += align_up(parts[k]);
   }
   a.flags = static_cast<uint32_t*>(ptr[0]);
   a.stats = static_cast<uint32_t*>(ptr[1]);
-  a.keys = static_cast<uint32_t*>(ptr[2]);
-  a.unc = static_cast<uint32_t*>(ptr[3]);
-  a.part_o = static_cast<float*>(ptr[4]);
-  a.part_ml = static_cast<float*>(ptr[5]);
+  a.cnts = static_cast<uint32_t*>(ptr[2]);
+  a.keys = static_cast<uint32_t*>(ptr[3]);
+  a.band = static_cast<uint32_t*>(ptr[4]);
+  a.part_o = static_cast<float*>(ptr[5]);
+  a.part_ml = static_cast<float*>(ptr[6]);
   a.R = num_requests;
   a.H = cfg->num_kv_heads;
   a.G = cfg->group_size;
@@ -430,6 +431,7 @@ resa_status resa_sparse_step(const resa_config* cfg, const resa_paged_kv* kv, in
   a.num_pool_blocks = kv->num_pool_blocks;
   a.mode = cfg->score_mode;
   a.key_stride = key_stride_for(kv->max_blocks);
+  a.band_stride = step_band_stride(cfg->dtype, cfg->head_dim, num_requests, cfg->num_kv_heads, kv->max_blocks);
   a.max_sel = max_sel;
   a.budget_num = cfg->budget_num;
   a.budget_den = cfg->budget_den;
@@ -437,11 +439,13 @@ resa_status resa_sparse_step(const resa_config* cfg, const resa_paged_kv* kv, in
   a.local_blocks = cfg->local_blocks;
   a.scale_log2 = scale_log2(cfg);
   step_geometry(cfg->dtype, cfg->head_dim, num_requests, cfg->num_kv_heads, kv->max_blocks, &a.unroll, &a.nslices);
-  // one workgroup per compute unit at most: every workgroup of the grid is
-  // resident at once, which the waits of the attention phase rely on
+  // One workgroup per compute unit at most: every workgroup of the grid is
+  // resident at once, and the slices of a row fit in one sweep of the grid,
+  // which the waits between the slices of a row rely on.
   const long long units = (long long)num_requests * cfg->num_kv_heads * a.nslices;
   if (units > 0x7fffffffLL) return RESA_ERR_UNSUPPORTED;
   a.grid = (int)(units < cus ? units : cus);
+  if (a.nslices > a.grid) return RESA_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return from_hip(launch_step(a, static_cast<hipStream_t>(stream)));
 }

@@ -110,22 +110,27 @@ struct StepArgs {
   int32_t* sel_idx;
   int32_t* sel_cnt;
   float* out;
-  uint32_t* flags;  // [1 + R * H * 4][32] counters and state words, zero between calls
+  uint32_t* flags;  // [R][H][5][32] counters and state words, zero between calls
   uint32_t* stats;  // [R][H][W][4] per-slice key statistics
+  uint32_t* cnts;   // [R][H][W][4] per-slice counts
   uint32_t* keys;   // [R][H][key_stride]
-  uint32_t* unc;    // [R][H][max_sel] selected blocks decided by the exact selection only
+  uint32_t* band;   // [R][H][band_stride][2] band keys and their block ids, by slice
   float* part_o;    // [R][H][W][G][D]
   float* part_ml;   // [R][H][W][G][2]
-  int32_t R, H, G, D, dtype, max_blocks, num_pool_blocks, mode, key_stride, max_sel;
+  int32_t R, H, G, D, dtype, max_blocks, num_pool_blocks, mode, key_stride, band_stride, max_sel;
   int32_t budget_num, budget_den, min_blocks, local_blocks;
   float scale_log2;
   int32_t unroll, nslices, grid;  // from step_geometry / the launcher
 };
 // Slices of the step: passes per slice (unroll) and slices per (request,
-// KV head) (nslices) for these sizes.
+// KV head).
 void step_geometry(int dtype, int D, int R, int H, int max_blocks, int* unroll, int* nslices);
+// Band entries per (request, KV head): slices times blocks per slice.
+int step_band_stride(int dtype, int D, int R, int H, int max_blocks);
+constexpr int kStepParts = 7;
 // Bytes of each workspace part of the step, in the order of StepArgs.
-void step_workspace_parts(int dtype, int D, int R, int H, int G, int max_blocks, int max_sel, size_t parts[6]);
+void step_workspace_parts(int dtype, int D, int R, int H, int G, int max_blocks, int max_sel,
+                          size_t parts[kStepParts]);
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 
 struct DecodeArgs {

@@ -77,7 +77,6 @@ __global__ __launch_bounds__(kNT) void score_select_kernel(const ScoreArgs a) {
   uint32_t kmin = ss.kmin, kmax = ss.kmax;
   wave_min_max(kmin, kmax);
   if (lane == 0) s_mm[wave] = make_uint2(kmin, kmax);
-  wait_vm_all();
   __syncthreads();
   uint32_t* counter = a.sync + ((size_t)r * H + i) * kSyncWords;
   uint32_t* ranges = a.ranges + ((size_t)r * H + i) * a.range_stride;
@@ -90,7 +89,10 @@ __global__ __launch_bounds__(kNT) void score_select_kernel(const ScoreArgs a) {
     }
     store_agent(ranges + 2 * slice, ~mn);
     store_agent(ranges + 2 * slice + 1, mx);
-    wait_vm_all();
+  }
+  wait_vm_all();  // this thread's key (and range) stores are complete
+  __syncthreads();
+  if (t == 0) {
     const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = old == (uint32_t)(a.nslices - 1);
     if (last) store_agent(counter, 0u);  // every workgroup of the row has arrived: reset for the next call

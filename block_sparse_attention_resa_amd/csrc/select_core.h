@@ -1,5 +1,5 @@
 // Top-n block selection over order-preserving 32-bit score keys, run by one
-// 1024-thread workgroup per (request, KV head), and the device-scope
+// workgroup per (request, KV head), and the device-scope
 // exchange helpers of the kernels that hand keys from workgroup to
 // workgroup inside one launch.
 //
@@ -8,13 +8,13 @@
 // block id).
 //
 // Thread t owns the consecutive candidate blocks [k t, k t + k) (16-byte
-// loads, kept in registers; rows longer than 32768 blocks fall back to blocks
-// t, t + 1024, ... re-read from memory).  The k-th largest key is found by
+// loads, kept in registers; rows longer than 32 keys per thread fall back to
+// blocks t, t + NT, ... re-read from memory).  The k-th largest key is found by
 // histogram passes in LDS over monotone bin maps: the first pass bins the
 // candidates' range into 4096 equal-width bins, later passes (rarely needed)
 // bin the key offsets inside the boundary bucket.  Once the boundary bucket
-// holds at most 256 keys they are packed into LDS and ranked, sixteen lanes
-// per member.  Blocks above the threshold are taken, blocks equal to it
+// holds at most 256 keys they are packed into LDS and each is ranked against
+// all of them by one thread.  Blocks above the threshold are taken, blocks equal to it
 // lowest index first, and one scan of the per-thread counts places every
 // selected id in ascending order.  Wave-wide scans and reductions use DPP
 // lane shifts, and wavefronts whose keys are all candidates run every
@@ -60,7 +60,6 @@ __device__ __forceinline__ void wait_vm_all() {
 constexpr int kDigitBits = 12;  // histogram pass: 4096 bins
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kFinishMax = 256;  // boundary bucket size the ranking finish takes
-constexpr int kRankLanes = 16;   // lanes (one DPP row) that rank one bucket member
 
 // Cross-lane steps through DPP (row shifts within 16-lane rows, then the
 // row-15 / row-31 broadcasts), which stay in the vector ALU instead of the
@@ -318,43 +317,37 @@ struct Bucket {
   __device__ bool has(uint32_t x) const { return x >= lo && x <= hi && (bin < 0 || map(x) == bin); }
 };
 
-// Sum of an int over the sixteen lanes of a DPP row, in every lane of the row.
-__device__ __forceinline__ int row16_sum(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false);  // row_ror:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x124, 0xf, 0xf, false);  // row_ror:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x122, 0xf, 0xf, false);  // row_ror:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x121, 0xf, 0xf, false);  // row_ror:1
-  return x;
-}
-
 // LDS of the selection by an NT-thread workgroup.
 template <int NT>
 struct SelectLds {
   uint32_t hist2[2][kBins + 1];  // alternating pass histograms; the last slot takes non-members
   WaveSlots<int, NT / 64> scan_slots;
   WaveSlots<uint2, NT / 64> mm_slots;
-  uint32_t bucket[kFinishMax];
+  __align__(16) uint32_t bucket[kFinishMax + 8];  // read eight at a time
   int bc2[2][3];  // boundary record of a pass (bin, rank left, keys), by pass parity
   int packed;     // keys of the boundary bucket packed so far
 };
 
-// Top-k of the C candidate keys of one row (k in (0, C)) held by `kr`
-// (prefetched, count set), whose range [mn, mx] is known: writes the k
-// selected block ids, ascending, to out.  With unc_out (uniform) it also
-// writes, ascending, the selected ids whose key is at most t_hi and returns
-// their number (0 without unc_out).  Expects the two histograms and
-// `packed` cleared and published by a barrier.  Every thread of the
-// workgroup calls it.
+// The k-th largest key `thr` of a row: every key above it is selected, and
+// of the n_eq keys equal to it the take_eq lowest block ids.
+struct Threshold {
+  uint32_t thr;
+  int take_eq, n_eq;
+};
+
+// Threshold of the top-k of the C candidate keys of one row (k in (0, C))
+// held by `kr` (prefetched, count set), whose range [mn, mx] is known.
+// Expects the two histograms and `packed` cleared and published by a
+// barrier.  `scan_use` carries the parity of the exchange slots to the
+// caller's later scans.  Every thread of the workgroup calls it.
 template <int NT, int KPT>
-__device__ __forceinline__ int select_top(SelectLds<NT>& sl, KeyRuns<NT, KPT>& kr, int C, int k, uint32_t mn,
-                                          uint32_t mx, int32_t* __restrict__ out, uint32_t t_hi = 0u,
-                                          uint32_t* __restrict__ unc_out = nullptr) {
+__device__ __forceinline__ Threshold select_threshold(SelectLds<NT>& sl, KeyRuns<NT, KPT>& kr, int C, int k,
+                                                      uint32_t mn, uint32_t mx, int& scan_use) {
   constexpr int BPT = kBins / NT;                   // histogram bins per thread in the scan (4 or 8)
   constexpr bool kKeepBins = KPT > 0 && KPT * NT <= 16 * 1024;  // first-pass bins kept in registers (16 bits each)
   static_assert(BPT == 4 || BPT == 8, "the scan reads four or eight bins per thread");
-  int scan_use = 0, mm_use = 0;  // alternating slot sets, identical in every thread
+  int mm_use = 0;  // alternating slot sets, identical in every thread
   const int tid = threadIdx.x;
-  const int R = kr.nrounds();
 
   Bucket bk;
   bk.lo = mn;
@@ -459,10 +452,10 @@ __device__ __forceinline__ int select_top(SelectLds<NT>& sl, KeyRuns<NT, KPT>& k
     take_eq = remaining;
     n_eq = bucket_n;
   } else if (bucket_n <= kFinishMax) {
-    // Ranking finish: the bucket's keys are packed into LDS (slots handed out
-    // by an LDS counter: their order does not matter), then sixteen lanes
-    // rank each member against a sixteenth of the others each; the member
-    // whose rank range holds `remaining` is the threshold.
+    // Ranking finish: the bucket's keys are packed into LDS (their order does
+    // not matter), then thread m ranks
+    // member m against all of them; the member whose rank range holds
+    // `remaining` is the threshold.
     bool kept = false;
     if constexpr (kKeepBins) kept = npass == 1;
     if constexpr (KPT > 0) {
@@ -481,8 +474,11 @@ __device__ __forceinline__ int select_top(SelectLds<NT>& sl, KeyRuns<NT, KPT>& k
       } else {
         RESA_FOR_KEYS({ mem |= (in && bk.has(kr.key(j)) ? 1u : 0u) << j; });
       }
+      // slots by a scan of the per-thread counts (same-address LDS atomics
+      // would serialize)
+      int n_mem;
+      int pos = block_exclusive_scan<NT>(__popc(mem), sl.scan_slots, scan_use, n_mem);
       if (mem != 0u) {
-        int pos = atomicAdd(&sl.packed, __popc(mem));
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
           if ((mem >> j) & 1u) {
@@ -502,19 +498,24 @@ __device__ __forceinline__ int select_top(SelectLds<NT>& sl, KeyRuns<NT, KPT>& k
     __syncthreads();
     const int nb = bucket_n;  // the members counted by the last pass
     int* bc = sl.bc2[npass & 1];  // the record the last pass did not use
-    const int sub = tid % kRankLanes;
-    for (int m0 = 0; m0 < nb; m0 += NT / kRankLanes) {  // uniform: every lane of a DPP row takes part
-      const int m = m0 + tid / kRankLanes;
-      const uint32_t x = sl.bucket[m < nb ? m : 0];
+    static_assert(kFinishMax <= NT, "one bucket member per thread");
+    if (tid < nb) {
+      // member tid against every member, eight per step (two 16-byte reads
+      // that every lane makes alike)
+      const uint32_t x = sl.bucket[tid];
       int gt = 0, eq = 0;
-      for (int qq = sub; qq < nb; qq += kRankLanes) {
-        const uint32_t y = sl.bucket[qq];
-        gt += y > x ? 1 : 0;
-        eq += y == x ? 1 : 0;
+      for (int s0 = 0; s0 < nb; s0 += 8) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&sl.bucket[s0]);
+        const uint4 b = *reinterpret_cast<const uint4*>(&sl.bucket[s0 + 4]);
+        const uint32_t y[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool in = s0 + e < nb;
+          gt += in && y[e] > x ? 1 : 0;
+          eq += in && y[e] == x ? 1 : 0;
+        }
       }
-      gt = row16_sum(gt);
-      eq = row16_sum(eq);
-      if (sub == 0 && m < nb && gt < remaining && remaining <= gt + eq) {  // every writer stores the same values
+      if (gt < remaining && remaining <= gt + eq) {  // every writer stores the same values
         bc[0] = (int)x;
         bc[1] = remaining - gt;
         bc[2] = eq;
@@ -537,6 +538,53 @@ __device__ __forceinline__ int select_top(SelectLds<NT>& sl, KeyRuns<NT, KPT>& k
     take_eq = bucket_n;
     n_eq = bucket_n;
   }
+  return Threshold{thr, take_eq, n_eq};
+}
+
+// Position, in the key order of `kr`, of the take_eq-th key equal to thr
+// (take_eq >= 1 of them exist).  Every thread calls it and gets the result.
+template <int NT, int KPT>
+__device__ __forceinline__ int cut_position(SelectLds<NT>& sl, KeyRuns<NT, KPT>& kr, uint32_t thr, int take_eq,
+                                            int& scan_use) {
+  const int tid = threadIdx.x;
+  int* res = &sl.bc2[0][0];
+  if constexpr (KPT > 0) {
+    uint32_t equal = 0;
+    RESA_FOR_KEYS({ equal |= (in && kr.key(j) == thr ? 1u : 0u) << j; });
+    int n_all;
+    const int before = block_exclusive_scan<NT>(__popc(equal), sl.scan_slots, scan_use, n_all);
+    if (before < take_eq && take_eq <= before + __popc(equal)) {
+      uint32_t m = equal;
+      for (int q = before + 1; q < take_eq; ++q) m &= m - 1u;
+      *res = tid * KPT + __builtin_ctz(m);
+    }
+  } else {
+    int base = 0;
+    for (int j = 0; j < kr.rounds; ++j) {
+      const bool e = kr.valid(j) && kr.key(j) == thr;
+      int tot;
+      const int pos = block_exclusive_scan<NT>(e ? 1 : 0, sl.scan_slots, scan_use, tot);
+      if (e && base + pos + 1 == take_eq) *res = tid + j * NT;
+      base += tot;
+    }
+  }
+  __syncthreads();
+  return *res;
+}
+
+// Top-k of the C candidate keys of one row (k in (0, C)) held by `kr`
+// (prefetched, count set), whose range [mn, mx] is known: writes the k
+// selected block ids, ascending, to out.  Expects the two histograms and
+// `packed` cleared and published by a barrier.  Every thread of the
+// workgroup calls it.
+template <int NT, int KPT>
+__device__ __forceinline__ void select_top(SelectLds<NT>& sl, KeyRuns<NT, KPT>& kr, int C, int k, uint32_t mn,
+                                           uint32_t mx, int32_t* __restrict__ out) {
+  int scan_use = 0;
+  const int tid = threadIdx.x;
+  const Threshold th = select_threshold<NT, KPT>(sl, kr, C, k, mn, mx, scan_use);
+  const uint32_t thr = th.thr;
+  const int take_eq = th.take_eq, n_eq = th.n_eq;
 
   // Output in ascending block order.  Each thread's keys are consecutive
   // blocks, so one scan of the per-thread counts gives every thread its first
@@ -562,19 +610,10 @@ __device__ __forceinline__ int select_top(SelectLds<NT>& sl, KeyRuns<NT, KPT>& k
     const int first = tid * KPT;
     for (uint32_t m = take; m != 0u; m &= m - 1u, ++pos)
       if (pos < k) out[pos] = first + __builtin_ctz(m);
-    int n_unc = 0;
-    if (unc_out) {
-      uint32_t above = 0;
-      RESA_FOR_KEYS({ above |= (in && kr.key(j) > t_hi ? 1u : 0u) << j; });
-      const uint32_t unc = take & ~above;
-      int upos = block_exclusive_scan<NT>(__popc(unc), sl.scan_slots, scan_use, n_unc);
-      for (uint32_t m = unc; m != 0u; m &= m - 1u, ++upos)
-        if (upos < k) store_agent(unc_out + upos, (uint32_t)(first + __builtin_ctz(m)));
-    }
-    return n_unc;
   } else {
     // Any number of rounds: one block scan per round.
-    int base_out = 0, base_eq = 0, base_unc = 0;
+    const int R = kr.nrounds();
+    int base_out = 0, base_eq = 0;
     for (int j = 0; j < R; ++j) {
       const bool v = kr.valid(j);
       const uint32_t x = kr.key(j);
@@ -585,110 +624,10 @@ __device__ __forceinline__ int select_top(SelectLds<NT>& sl, KeyRuns<NT, KPT>& k
       int tot;
       const int pos = block_exclusive_scan<NT>(t ? 1 : 0, sl.scan_slots, scan_use, tot);
       if (t && base_out + pos < k) out[base_out + pos] = tid + j * NT;
-      if (unc_out) {
-        const bool u = t && x <= t_hi;
-        int tot_u;
-        const int upos = block_exclusive_scan<NT>(u ? 1 : 0, sl.scan_slots, scan_use, tot_u);
-        if (u && base_unc + upos < k) store_agent(unc_out + base_unc + upos, (uint32_t)(tid + j * NT));
-        base_unc += tot_u;
-      }
       base_out += tot;
       base_eq += tot_eq;
     }
-    return base_unc;
   }
-}
-
-// ------------------------------------------------------------ band select
-//
-// The top-k with a known bracket of the threshold: given lo <= thr <= hi,
-// where thr is the k-th largest candidate key and fewer than k keys exceed
-// hi, every key above hi is taken, no key below lo is, and only the keys in
-// [lo, hi] (the band) need ranking.  The band is packed into LDS in
-// ascending block order (so a lower slot is a lower block id) and the
-// (k - #above)-th largest of it is found by select_top on the packed keys.
-
-constexpr int kBandMax = 4096;  // band keys the LDS holds
-
-struct BandLds {
-  __align__(16) uint32_t key[kBandMax];  // band keys, ascending block order
-  int id[kBandMax];                       // their block ids
-  int slot[kBandMax];                     // selected band slots, ascending
-  uint32_t taken[kBandMax / 32];          // bit per band slot
-};
-
-// Writes the k selected block ids of the C candidates held by `kr`
-// (prefetched, count set; KPT > 0), ascending, to out, and the selected ids
-// whose key is at most hi, ascending, to unc_out (device-scope stores);
-// returns their number.  Returns -1, having written nothing, when the band
-// holds more than kBandMax keys.  Expects the two histograms and `packed` of
-// `sl` cleared and published by a barrier.  Every thread calls it.
-template <int NT, int KPT>
-__device__ __forceinline__ int select_band(SelectLds<NT>& sl, BandLds& bl, KeyRuns<NT, KPT>& kr, int k,
-                                           uint32_t lo, uint32_t hi, int32_t* __restrict__ out,
-                                           uint32_t* __restrict__ unc_out) {
-  static_assert(KPT > 0 && NT * KPT <= 16384, "register-held keys; counts fit in 16 bits");
-  constexpr int KPB = kBandMax / NT;  // band keys per thread in the band selection
-  static_assert(KPB % 4 == 0 && KPB <= 32, "band keys are read four at a time");
-  int scan_use = 0;
-  const int tid = threadIdx.x;
-  const int first = tid * KPT;
-  uint32_t above = 0, band = 0;
-  RESA_FOR_KEYS({
-    const uint32_t x = kr.key(j);
-    above |= (in && x > hi ? 1u : 0u) << j;
-    band |= (in && x >= lo && x <= hi ? 1u : 0u) << j;
-  });
-  for (int q = tid; q < kBandMax / 32; q += NT) bl.taken[q] = 0u;
-  int tot;
-  const int pre = block_exclusive_scan<NT>((__popc(band) << 16) | __popc(above), sl.scan_slots, scan_use, tot);
-  const int nb = tot >> 16;
-  const int k2 = k - (tot & 0xffff);  // keys to take from the band: 1 <= k2 <= nb
-  if (nb > kBandMax || k2 < 1 || k2 > nb) return -1;  // uniform
-  const int p0 = pre >> 16;  // this thread's first band slot
-  {
-    int pos = p0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if ((band >> j) & 1u) {
-        bl.key[pos] = kr.key(j);
-        bl.id[pos] = first + j;
-        ++pos;
-      }
-    }
-  }
-  __syncthreads();
-  if (k2 == nb) {
-    for (int q = tid; q < nb; q += NT) bl.slot[q] = q;
-  } else {
-    KeyRuns<NT, KPB> kb;
-    kb.load_lds(bl.key);
-    kb.set_count(nb);
-    select_top<NT, KPB>(sl, kb, nb, k2, lo, hi, bl.slot);
-  }
-  __syncthreads();
-  for (int q = tid; q < k2; q += NT) {
-    const int sl_q = bl.slot[q];
-    atomicOr(&bl.taken[sl_q >> 5], 1u << (sl_q & 31));
-    store_agent(unc_out + q, (uint32_t)bl.id[sl_q]);
-  }
-  __syncthreads();
-  uint32_t take = above;
-  {
-    int pos = p0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if ((band >> j) & 1u) {
-        take |= ((bl.taken[pos >> 5] >> (pos & 31)) & 1u) << j;
-        ++pos;
-      }
-    }
-  }
-  int n_all;
-  int pos = block_exclusive_scan<NT>(__popc(take), sl.scan_slots, scan_use, n_all);
-  for (uint32_t m = take; m != 0u; m &= m - 1u, ++pos)
-    if (pos < k) out[pos] = first + __builtin_ctz(m);
-  return k2;
 }
 
 }  // namespace resa

@@ -1,8 +1,9 @@
 """GPU parity at the full sizes of the five measured workloads, in the launch
 configuration bench.py times (automatic split counts), checked against the
 CPU oracle on every output the oracle can afford (whole layers for the 32K
-and ragged batches, two of the 28 layers at 256K, sampled rectification
-rows at 128K), plus HIP-graph replay of the timed step."""
+and ragged batches, two of the 28 layers at 256K, every rectification row of
+one 128K request and sampled rows of the others), the sweep's budgets at
+64K, plus HIP-graph replay of the timed step against the oracle."""
 
 import numpy as np
 import pytest
@@ -75,10 +76,26 @@ def test_qwen7b_ctx256k_layer(layer):
     print(f"layer {layer}: near-tie swaps {swaps}")
 
 
+def step_against_oracle(case, sel_idx, sel_cnt, out, tag):
+    """Selection and sparse outputs of one layer-step against the oracle."""
+    lists = C.sel_lists(sel_idx, sel_cnt)
+    g = case.spec.group_size
+    scale = C.sm_scale(case.cfg)
+    for r in range(case.R):
+        L = case.inp.seq_lens[r]
+        for i in range(case.spec.num_kv_heads):
+            K, V, q = C.keys_of(case, r, i), C.values_of(case, r, i), C.group_q(case, r, i)
+            lo, hi = O.descriptors(K, L)
+            C.check_selection(O.scores(q, lo, hi), lists[r][i], case.cfg, tag=f"{tag} r{r} i{i}")
+            C.check_out(out[r, i * g:(i + 1) * g].cpu().numpy(), O.attend(q, K, V, L, lists[r][i], scale),
+                        f"{tag} r{r} i{i}")
+
+
 def test_graph_replay_matches_eager():
     """The timed step (score/select with tail refresh + sparse decode over
     several layers) captured in a HIP graph: every replay, with eager work and
-    synchronisations in between, reproduces the eager results bit for bit."""
+    synchronisations in between, reproduces the eager results bit for bit,
+    and every replay's selections and outputs match the oracle."""
     spec = WORKLOADS["qwen7b_ctx32k_b1"]
     cases = [C.make_case(spec, seed=300 + l) for l in range(3)]
     R, H, g, d = 1, spec.num_kv_heads, spec.group_size, spec.head_dim
@@ -122,6 +139,34 @@ def test_graph_replay_matches_eager():
         for st, (si, o) in zip(state, eager):
             assert torch.equal(st["sel_idx"], si), f"replay {rep}: selection differs"
             assert torch.equal(st["out"], o), f"replay {rep}: output differs"
+            step_against_oracle(st["case"], st["sel_idx"], st["sel_cnt"], st["out"], f"replay {rep}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("budget", [(1, 50), (1, 20), (1, 5)])
+def test_budget_sweep_64k(budget):
+    """The budgets of the context x budget sweep besides 1/10, at 64K
+    (4096 blocks per KV head; 82, 205 and 820 of them chosen): score/select +
+    sparse decode and the persistent step, selections and outputs against the
+    oracle, and the two paths against each other."""
+    num, den = budget
+    spec = WORKLOADS["qwen7b_ctx32k_b1"].with_(seq_lens=(65536,), budget_num=num, budget_den=den)
+    case = C.make_case(spec, seed=640 + den)
+    C.run_descriptors(case)
+    sel_idx, sel_cnt, _ = C.run_score_select(case, with_scores=False)
+    out = C.run_sparse(case, sel_idx, sel_cnt)
+    torch.cuda.synchronize()
+    assert int(sel_cnt[0, 0]) == O.selection_count(4096, num, den, spec.min_blocks, spec.local_blocks)
+    step_against_oracle(case, sel_idx, sel_cnt, out, f"rho {num}/{den}")
+    ms = C.max_sel_for(case)
+    si2 = torch.full_like(sel_idx, -3)
+    sc2 = torch.full_like(sel_cnt, -3)
+    out2 = torch.full_like(out, float("nan"))
+    ws = resa.alloc_workspace(case.cfg, resa.OP_SPARSE_STEP, case.R, case.kv.max_blocks, ms)
+    resa.sparse_step(case.cfg, case.kv, case.inp.q, si2, sc2, out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(si2, sel_idx) and torch.equal(sc2, sel_cnt)
+    C.check_out(out2.cpu().numpy(), out.cpu().numpy().astype(np.float64), f"rho {num}/{den} step vs two calls")
 
 
 @pytest.mark.timeout(900)
@@ -197,6 +242,15 @@ def test_qwen7b_ctx131k_b4_sparse_then_rectify():
             Kr, Vr = K[r][i].astype(np.float64), V[r][i].astype(np.float64)
             # descriptors: every block equals a rebuild of the rectified cache
             C.check_descriptors(case, r, i, Kr, L)
+            if r == 0:
+                # request 0: every chunk row (all 448 query rows of the KV
+                # head) against the oracle's rectification, which writes the
+                # chunk's rows and attends causally for each of them
+                ref, _, _, _, _, _ = O.rectify(C.np64(qc[r, :, i * g:(i + 1) * g]), C.np64(kn[r, :, i]),
+                                               C.np64(vn[r, :, i]), Kr, Vr, L, scale)
+                for t in range(f):
+                    C.check_out(rout[r, t, i * g:(i + 1) * g].cpu().numpy(), ref[t], f"rectify r{r} i{i} t{t}")
+                continue
             for t in (0, f // 2 - 1, f - 1):  # sampled chunk rows, all heads of the group
                 ref = O.dense(C.np64(qc[r, t, i * g:(i + 1) * g]), Kr, Vr, P + t + 1, scale)
                 C.check_out(rout[r, t, i * g:(i + 1) * g].cpu().numpy(), ref, f"rectify r{r} i{i} t{t}")
