@@ -115,10 +115,8 @@ size_t partial_bytes(const resa_config* c, int R, int S, long long rows_per_head
 
 size_t workspace_bytes(const resa_config* c, int op, int R, int max_blocks, int max_sel, int chunk) {
   switch (op) {
-    case RESA_OP_SCORE_SELECT:  // arrival counters, slice key ranges, then the score keys
-      return align_up(score_select_sync_bytes(R, c->num_kv_heads)) +
-             align_up(score_select_range_bytes(R, c->num_kv_heads, max_blocks)) +
-             align_up((size_t)R * c->num_kv_heads * key_stride_for(max_blocks) * sizeof(uint32_t));
+    case RESA_OP_SCORE_SELECT:  // the score keys
+      return align_up((size_t)R * c->num_kv_heads * key_stride_for(max_blocks) * sizeof(uint32_t));
     case RESA_OP_SPARSE_DECODE:
     case RESA_OP_DENSE_DECODE: {
       const int S = splits_for(c, op, R, max_blocks, max_sel, chunk);
@@ -287,11 +285,7 @@ resa_status resa_score_select(const resa_config* cfg, const resa_paged_kv* kv, i
   sa.refresh_tail = refresh_tail != 0;
   sa.table = kv->block_table;
   sa.seq_lens = kv->seq_lens;
-  const size_t sync_b = align_up(score_select_sync_bytes(num_requests, cfg->num_kv_heads));
-  const size_t range_b = align_up(score_select_range_bytes(num_requests, cfg->num_kv_heads, kv->max_blocks));
-  sa.sync = static_cast<uint32_t*>(ws);
-  sa.ranges = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sync_b);
-  sa.keys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sync_b + range_b);
+  sa.keys = static_cast<uint32_t*>(ws);
   sa.scores = scores;
   sa.sel_idx = sel_idx;
   sa.sel_cnt = sel_cnt;

@@ -77,8 +77,6 @@ struct ScoreArgs {
   int32_t refresh_tail;
   const int32_t* table;
   const int32_t* seq_lens;
-  uint32_t* sync;    // [R][H] arrival counters (128-byte lines), zero between calls
-  uint32_t* ranges;  // [R][H][range_stride] per-slice key ranges
   uint32_t* keys;  // [R][H][key_stride] workspace
   float* scores;   // nullable export [R][H][max_blocks]
   int32_t* sel_idx;
@@ -86,13 +84,9 @@ struct ScoreArgs {
   int32_t R, H, G, D, dtype, max_blocks, num_pool_blocks, mode;
   int32_t key_stride;  // key_stride_for(max_blocks)
   int32_t max_sel, budget_num, budget_den, min_blocks, local_blocks;
-  int32_t nslices, unroll, range_stride;  // set by the launcher
 };
+// The scoring launch, then the selection launch.
 hipError_t launch_score_select(const ScoreArgs& a, hipStream_t stream);
-// Bytes of the arrival counters of R x H rows (zero between calls) and of
-// their per-slice key ranges.
-size_t score_select_sync_bytes(int R, int H);
-size_t score_select_range_bytes(int R, int H, int max_blocks);
 
 // Row stride of the score keys: a multiple of 4 entries, so every row starts
 // 16-byte aligned and the selection can read its keys with 16-byte loads.

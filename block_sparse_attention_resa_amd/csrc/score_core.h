@@ -1,5 +1,6 @@
-// Group block scores of one slice of consecutive blocks (Eq 4 of the
-// "Rectified Sparse Attention" analysis page, paper-graph-ui, §3.4.1).
+// Group block scores (Eq 4 of the "Rectified Sparse Attention" analysis
+// page, paper-graph-ui, §3.4.1): descriptor chunk loads, the DPP group sums,
+// and the scoring of one slice of consecutive blocks by a workgroup.
 //
 // For one GQA group the score of block b sums, over the group's query heads
 // j and channels c, max(q_jc * lo_bc, q_jc * hi_bc).  Because hi >= lo this
@@ -24,6 +25,11 @@ struct ChunkLoad;
 template <>
 struct ChunkLoad<bf16_t> {
   static constexpr int kVals = 16;  // bf16 values per 32-byte chunk
+  using Pair = uint32_t;            // two consecutive channels
+  __device__ static void unpack_pair(uint32_t w, float& a, float& b) {
+    a = bf16_lo_f32(w);
+    b = bf16_hi_f32(w);
+  }
   __device__ static void unpack(const uint4& a, const uint4& b, float* f) {
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -37,6 +43,11 @@ struct ChunkLoad<bf16_t> {
 template <>
 struct ChunkLoad<float> {
   static constexpr int kVals = 8;
+  using Pair = uint2;
+  __device__ static void unpack_pair(uint2 w, float& a, float& b) {
+    a = __uint_as_float(w.x);
+    b = __uint_as_float(w.y);
+  }
   __device__ static void unpack(const uint4& a, const uint4& b, float* f) {
     f[0] = __uint_as_float(a.x);
     f[1] = __uint_as_float(a.y);

@@ -1,194 +1,305 @@
-// resa_score_select in one launch: group block scores (Eq 4) and top-n
-// block selection (Eq 5 with the forced local window) of the "Rectified
-// Sparse Attention" analysis page (paper-graph-ui), §3.4.1.
+// resa_score_select: group block scores (Eq 4) and top-n block selection
+// (Eq 5 with the forced local window) of the "Rectified Sparse Attention"
+// analysis page (paper-graph-ui), §3.4.1, in two launches.
 //
-// A 1024-thread workgroup scores one slice of consecutive blocks of one
-// (request, KV head) (score_core.h), writes the scores as order-preserving
-// keys, stores the slice's candidate key range in its own slot and counts
-// itself in with one atomic add.  The workgroup that arrives last for a
-// (request, KV head) - every key of the row is written by then - runs the
-// selection (select_core.h) with its 1024 threads while the others have
-// exited, so the selection costs no launch of its own.  The last workgroup
-// resets the counter to zero for the next call.  One extra workgroup per
-// (request, KV head) refreshes the tail block's descriptor when asked.
+// Scoring.  A workgroup scores a run of consecutive blocks for a group of KV
+// heads of one request: thread -> (block, head, 32-byte descriptor chunk) is
+// fixed, so one table entry per block serves all heads of the group and the
+// heads' descriptors of a block, adjacent in the pool, are read together.
+// Each thread folds its share of the group's queries into the coefficients
+// (N, P) (score_core.h) once, then streams its descriptor chunks with one
+// fused multiply-add per stored value; CH lanes combine a descriptor with
+// DPP row rotations.  Scores are written as order-preserving 32-bit keys.
+// One extra workgroup per request refreshes the tail block's descriptor of
+// every KV head when asked (the block the newest token was appended to; it
+// is always selected, so the score read for it concurrently never matters).
+//
+// Selection.  One 1024-thread workgroup per (request, KV head) runs the
+// histogram select of select_core.h over that row's keys (sixteen
+// wavefronts: the selection is latency-bound on one CU, and more resident
+// wavefronts hide more of it than fewer, longer ones).  A second launch
+// rather than a last-arriving scoring workgroup: keeping the selection's
+// registers and LDS out of the scoring workgroups lets several of them share
+// a CU, and the fused form measured slower on every workload.
 #include "desc_unit.h"
 #include "score_core.h"
 
 namespace resa {
 namespace {
 
-constexpr int kNT = 1024;      // threads of a scoring / selection workgroup
-constexpr int kMaxUnroll = 4;  // passes of a scoring workgroup over its slice
+constexpr int kScoreUnroll = 4;     // blocks per thread (passes) in the scoring kernel
+constexpr int kScoreThreads = 256;  // threads of a scoring workgroup, at most
+constexpr int kSelectThreads = 1024;
 
-// Exchange records in the workspace.  Per (request, KV head): an arrival
-// counter, zero between calls, alone in a 128-byte line (counters of
-// different heads on one line slow each other's atomics down); then per
-// slice the complement of its smallest candidate key and its largest
-// candidate key (complement and value of an empty slice: 0).
-constexpr int kSyncWords = 32;
-constexpr int kMinSliceBlocks = 32;  // blocks of the smallest slice (fp32, d = 128, one pass)
-inline int max_slices(int max_blocks) { return (max_blocks + kMinSliceBlocks - 1) / kMinSliceBlocks; }
+template <typename T, int D, int MODE, int MAXG>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(
+    const T* __restrict__ q, const T* desc, const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
+    uint32_t* __restrict__ keys, float* __restrict__ scores, int H, int HW, int G, int max_blocks,
+    int num_pool_blocks, const T* __restrict__ k_pool, T* desc_tail, int score_wgs, int key_stride) {
+  using CL = ChunkLoad<T>;
+  constexpr int VPL = CL::kVals;
+  constexpr int CH = 2 * D / VPL;  // lanes per descriptor
+  constexpr int HALF = CH / 2;     // lanes per descriptor row
+  extern __shared__ float s_coef[];  // [HW][2][D]: N (min row) then P (max row)
 
-template <typename T, int D, int MAXG, int KPT>
-__global__ __launch_bounds__(kNT) void score_select_kernel(const ScoreArgs a) {
-  using SS = SliceScore<T, D, MAXG, kNT, kMaxUnroll>;
-  __shared__ __align__(16) float s_coef[2 * D];  // N (min row), then P (max row)
-  __shared__ uint2 s_mm[kNT / 64];
-  __shared__ int s_last;
-  __shared__ SelectLds<kNT> sl;
-
-  const int slice = blockIdx.x;
-  const int i = blockIdx.y;
-  const int r = blockIdx.z;
+  const int r = blockIdx.y;
+  const int h0 = blockIdx.z * HW;  // this workgroup's KV heads: [h0, h0 + HW)
   const int t = threadIdx.x;
-  const int H = a.H;
-  const int32_t* tab = a.table + (size_t)r * a.max_blocks;
-  if (slice >= a.nslices) {
-    // Tail refresh: one wavefront recomputes the descriptor of the head's last
-    // block (the block the newest token was appended to).  That block is
-    // always selected, so the score the scoring workgroups read for it
-    // concurrently is never used.
-    if (t >= 64) return;
-    const int L = clampi(a.seq_lens[r], 0, a.max_blocks * kBlock);
+  if ((int)blockIdx.x >= score_wgs) {
+    // tail refresh of the group's heads, one wavefront per head
+    const int L = clampi(seq_lens[r], 0, max_blocks * kBlock);
     const int M = (L + kBlock - 1) / kBlock;
     if (M == 0) return;
-    const int p = clampi(tab[M - 1], 0, a.num_pool_blocks - 1);
-    descriptor_unit<T, D>(static_cast<const T*>(a.k_pool) + ((size_t)p * H + i) * kBlock * D,
-                          static_cast<T*>(const_cast<void*>(a.desc_pool)) + ((size_t)p * H + i) * 2 * D,
-                          L - (M - 1) * kBlock);
+    const int p = clampi(table[(size_t)r * max_blocks + M - 1], 0, num_pool_blocks - 1);
+    for (int i = h0 + (t >> 6); i < min(H, h0 + HW); i += (int)(blockDim.x >> 6))
+      descriptor_unit<T, D>(k_pool + ((size_t)p * H + i) * kBlock * D, desc_tail + ((size_t)p * H + i) * 2 * D,
+                            L - (M - 1) * kBlock);
     return;
   }
   const int lane = t & 63;
-  const int wave = t >> 6;
-  const int L = clampi(a.seq_lens[r], 0, a.max_blocks * kBlock);
-  const int M = (L + kBlock - 1) / kBlock;
-  const int nl = a.local_blocks < M ? a.local_blocks : M;
-  const int C = M - nl;  // candidates: blocks [0, C)
-  uint32_t* key_row = a.keys + ((size_t)r * H + i) * a.key_stride;
-  float* score_row = a.scores ? a.scores + ((size_t)r * H + i) * a.max_blocks : nullptr;
-  SS ss;
-  ss.run(static_cast<const T*>(a.q) + ((size_t)r * H + i) * a.G * D, static_cast<const T*>(a.desc_pool), tab, M, C,
-         slice * a.unroll * SS::BPP, a.unroll, H, i, a.G, a.mode, a.max_blocks, a.num_pool_blocks, key_row,
-         score_row, s_coef);
+  const int grp = t / CH;
+  const int lg = t % CH;
+  const int part = lg / HALF;  // 0: min row, 1: max row
+  const int c0 = (lg % HALF) * VPL;
+  const int hl = grp % HW;  // head within the group
+  const int head = h0 + hl;
+  const bool head_ok = head < H;
+  const int bsub = grp / HW;
+  const int bpi = blockDim.x / (CH * HW);  // blocks per pass
+  const int wg_blocks = bpi * kScoreUnroll;
+  const int wg_b0 = blockIdx.x * wg_blocks;
+  uint32_t* key_row = keys + ((size_t)r * H + (head_ok ? head : 0)) * key_stride;
+  float* score_row = scores ? scores + ((size_t)r * H + (head_ok ? head : 0)) * max_blocks : nullptr;
 
-  // This slice's candidate key range goes to its own slot; then the
-  // workgroup counts itself in.  Every key and range store has completed
-  // (device scope) before the arrival atomic is issued.
-  uint32_t kmin = ss.kmin, kmax = ss.kmax;
-  wave_min_max(kmin, kmax);
-  if (lane == 0) s_mm[wave] = make_uint2(kmin, kmax);
-  __syncthreads();
-  uint32_t* counter = a.sync + ((size_t)r * H + i) * kSyncWords;
-  uint32_t* ranges = a.ranges + ((size_t)r * H + i) * a.range_stride;
-  if (t == 0) {
-    uint32_t mn = 0xffffffffu, mx = 0u;
+  // The request length (a scalar load) and the physical ids of this
+  // workgroup's blocks (one coalesced load per wavefront, handed to the lanes
+  // with a shuffle) are in flight together; the descriptor loads need both,
+  // so skipping blocks past the sequence end costs no extra wait and no
+  // descriptor past it is read (in a ragged batch the table is sized for the
+  // longest request).  Load order matters: the in-order vector-memory
+  // counter makes a wait for a load also wait for every load issued before
+  // it, so the table entries go out first, then the queries, then the
+  // descriptors.
+  const int seq_len = seq_lens[r];
+  int my_pid = 0;
+  if (lane < wg_blocks && wg_b0 + lane < max_blocks) my_pid = table[(size_t)r * max_blocks + wg_b0 + lane];
+  // Every thread folds channel pairs of the group's queries into (N, P); all
+  // G rows are loaded before any is used (rows past G re-read row G - 1 and
+  // are ignored).  This thread's first pair is loaded here; further pairs
+  // (only when the heads' channel pairs outnumber the threads) are folded
+  // after the descriptor loads are issued.
+  using Pair = typename CL::Pair;
+  const int nheads = min(HW, H - h0);
+  const int npairs = nheads * D / 2;
+  const int nthr = blockDim.x;
+  Pair qv[MAXG];
+  {
+    // branch-free (a thread past the last pair re-reads it), so no wait is
+    // placed at a join before the descriptor loads
+    const int v0 = t < npairs ? t : npairs - 1;
+    const T* qh = q + ((size_t)r * H * G + (size_t)(h0 + v0 / (D / 2)) * G) * D + (v0 % (D / 2)) * 2;
 #pragma unroll
-    for (int w = 0; w < kNT / 64; ++w) {
-      mn = min(mn, s_mm[w].x);
-      mx = max(mx, s_mm[w].y);
+    for (int j = 0; j < MAXG; ++j) qv[j] = *reinterpret_cast<const Pair*>(qh + (size_t)min(j, G - 1) * D);
+  }
+  const int L = clampi(seq_len, 0, max_blocks * kBlock);
+  const int M = (L + kBlock - 1) / kBlock;
+  uint4 buf[kScoreUnroll][2];
+  int bl[kScoreUnroll];
+#pragma unroll
+  for (int u = 0; u < kScoreUnroll; ++u) {
+    const int bo = u * bpi + bsub;
+    const int b = wg_b0 + bo;
+    bl[u] = b;
+    const int p = clampi(__shfl(my_pid, bo), 0, num_pool_blocks - 1);
+    if (b < M && head_ok) {
+      const uint4* src = reinterpret_cast<const uint4*>(desc + (((size_t)p * H + head) * 2 + part) * D + c0);
+      buf[u][0] = src[0];
+      buf[u][1] = src[1];
+    } else {
+      buf[u][0] = make_uint4(0, 0, 0, 0);
+      buf[u][1] = make_uint4(0, 0, 0, 0);
     }
-    store_agent(ranges + 2 * slice, ~mn);
-    store_agent(ranges + 2 * slice + 1, mx);
   }
-  wait_vm_all();  // this thread's key (and range) stores are complete
-  __syncthreads();
-  if (t == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old == (uint32_t)(a.nslices - 1);
-    if (last) store_agent(counter, 0u);  // every workgroup of the row has arrived: reset for the next call
-    s_last = last ? 1 : 0;
+  for (int v = t; v < npairs; v += nthr) {
+    const int hh = v / (D / 2);
+    const int c = (v % (D / 2)) * 2;
+    if (v != t) {  // rare: more channel pairs than threads
+      const T* qh = q + ((size_t)r * H * G + (size_t)(h0 + hh) * G) * D + c;
+#pragma unroll
+      for (int j = 0; j < MAXG; ++j) qv[j] = *reinterpret_cast<const Pair*>(qh + (size_t)min(j, G - 1) * D);
+    }
+    float p0 = 0.f, p1 = 0.f, n0 = 0.f, n1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXG; ++j) {
+      float x0, x1;
+      CL::unpack_pair(qv[j], x0, x1);
+      x0 = j < G ? x0 : 0.f;
+      x1 = j < G ? x1 : 0.f;
+      if constexpr (MODE == 0) {
+        p0 += fmaxf(x0, 0.f);
+        p1 += fmaxf(x1, 0.f);
+        n0 += fminf(x0, 0.f);
+        n1 += fminf(x1, 0.f);
+      } else {
+        p0 += x0;
+        p1 += x1;
+      }
+    }
+    if constexpr (MODE != 0) {
+      const float m0 = p0 / (float)G, m1 = p1 / (float)G;
+      p0 = fmaxf(m0, 0.f);
+      p1 = fmaxf(m1, 0.f);
+      n0 = fminf(m0, 0.f);
+      n1 = fminf(m1, 0.f);
+    }
+    s_coef[(hh * 2 + 0) * D + c] = n0;
+    s_coef[(hh * 2 + 0) * D + c + 1] = n1;
+    s_coef[(hh * 2 + 1) * D + c] = p0;
+    s_coef[(hh * 2 + 1) * D + c + 1] = p1;
   }
   __syncthreads();
-  if (!s_last) return;
+  float coef[VPL];
+  const int hc = head_ok ? hl : 0;
+#pragma unroll
+  for (int v = 0; v < VPL; v += 4) {
+    const floatx4_t c4 = *reinterpret_cast<const floatx4_t*>(&s_coef[(hc * 2 + part) * D + c0 + v]);
+    coef[v] = c4[0];
+    coef[v + 1] = c4[1];
+    coef[v + 2] = c4[2];
+    coef[v + 3] = c4[3];
+  }
 
-  // ---- the last workgroup of (r, i): the selection
-  int n = 0;
+#pragma unroll
+  for (int u = 0; u < kScoreUnroll; ++u) {
+    float vals[VPL];
+    CL::unpack(buf[u][0], buf[u][1], vals);
+    float acc = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) acc = fmaf(coef[v], vals[v], acc);
+    acc = group_sum<CH>(acc);
+    if (lg == 0 && head_ok && bl[u] < M) {
+      key_row[bl[u]] = f32_order_key(acc);
+      if (score_row) score_row[bl[u]] = acc;
+    }
+  }
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(const uint32_t* __restrict__ keys,
+                                                               const int32_t* __restrict__ seq_lens,
+                                                               int32_t* __restrict__ sel_idx,
+                                                               int32_t* __restrict__ sel_cnt, int H, int max_blocks,
+                                                               int max_sel, int budget_num, int budget_den,
+                                                               int min_blocks, int local_blocks, int key_stride) {
+  constexpr int NT = kSelectThreads;
+  __shared__ SelectLds<NT> sl;
+  const int i = blockIdx.x;
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x;
+  KeyRuns<NT, KPT> kr;
+  kr.prefetch(keys + ((size_t)r * H + i) * key_stride, key_stride);  // in flight with seq_lens
+  const int L = clampi(seq_lens[r], 0, max_blocks * kBlock);
+  const int M = (L + kBlock - 1) / kBlock;
+  int32_t* out = sel_idx + ((size_t)r * H + i) * max_sel;
+
+  int n = 0, nl = 0;
   if (M > 0) {
-    long long nn = ((long long)M * a.budget_num + a.budget_den - 1) / a.budget_den;
-    if (nn < a.min_blocks) nn = a.min_blocks;
-    if (nn < a.local_blocks) nn = a.local_blocks;
+    long long nn = ((long long)M * budget_num + budget_den - 1) / budget_den;
+    if (nn < min_blocks) nn = min_blocks;
+    if (nn < local_blocks) nn = local_blocks;
     if (nn > M) nn = M;
     n = (int)nn;
+    nl = local_blocks < M ? local_blocks : M;
   }
   const int k = n - nl;  // blocks chosen by score
-  int32_t* out = a.sel_idx + ((size_t)r * H + i) * a.max_sel;
-  for (int j = t; j < a.max_sel; j += kNT) {
+  const int C = M - nl;  // candidates: blocks [0, C)
+  for (int j = tid; j < max_sel; j += NT) {
     if (j >= n) out[j] = -1;
     else if (j >= k) out[j] = C + (j - k);  // forced recent blocks close the ascending list
   }
-  if (t == 0) a.sel_cnt[(size_t)r * H + i] = n;
+  if (tid == 0) sel_cnt[(size_t)r * H + i] = n;
   if (k == 0) return;
   if (k == C) {
-    for (int j = t; j < C; j += kNT) out[j] = j;
+    for (int j = tid; j < C; j += NT) out[j] = j;
     return;
   }
-  // keys and slice ranges in flight together
-  KeyRuns<kNT, KPT> kr;
-  kr.prefetch(key_row, a.key_stride);
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  for (int s2 = t; s2 < a.nslices; s2 += kNT) {
-    mn = min(mn, ~load_agent(ranges + 2 * s2));
-    mx = max(mx, load_agent(ranges + 2 * s2 + 1));
-  }
   kr.set_count(C);
-  wave_min_max(mn, mx);
-  if (lane == 0) s_mm[wave] = make_uint2(mn, mx);
-  for (int b = t; b <= kBins; b += kNT) {
+  for (int b = tid; b <= kBins; b += NT) {  // published by the barrier of block_min_max
     sl.hist2[0][b] = 0u;
     sl.hist2[1][b] = 0u;
   }
-  if (t == 0) sl.packed = 0;
-  __syncthreads();
-  mn = 0xffffffffu;
-  mx = 0u;
-#pragma unroll
-  for (int w = 0; w < kNT / 64; ++w) {
-    mn = min(mn, s_mm[w].x);
-    mx = max(mx, s_mm[w].y);
-  }
-  select_top<kNT, KPT>(sl, kr, C, k, mn, mx, out);
+  if (tid == 0) sl.packed = 0;
+  // key range of the candidates
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  RESA_FOR_KEYS({
+    const uint32_t x = kr.key(j);
+    mn = in ? min(mn, x) : mn;
+    mx = in ? max(mx, x) : mx;
+  });
+  int mm_use = 1;  // the slot set the selection's first range pass does not use
+  block_min_max<NT>(mn, mx, sl.mm_slots, mm_use);
+  select_top<NT, KPT>(sl, kr, C, k, mn, mx, out);
 }
 
 template <typename T, int D>
-hipError_t launch_t(const ScoreArgs& a0, hipStream_t stream) {
-  constexpr int BPP = SliceScore<T, D, 8, kNT, kMaxUnroll>::BPP;
-  ScoreArgs a = a0;
-  a.range_stride = 2 * max_slices(a.max_blocks);
-  // Slices of up to four passes, fewer while that leaves the launch short of
-  // about one workgroup per compute unit.
-  const long long units = (long long)a.R * a.H;
-  int U = kMaxUnroll;
-  while (U > 1 && units * ((a.max_blocks + BPP * U - 1) / (BPP * U)) < 256) U /= 2;
-  a.unroll = U;
-  a.nslices = (a.max_blocks + BPP * U - 1) / (BPP * U);
-  dim3 grid((unsigned)(a.nslices + (a.refresh_tail ? 1 : 0)), (unsigned)a.H, (unsigned)a.R);
-  const int cand_max = a.key_stride;
-#define RESA_SS_LAUNCH(MAXG, KPT) \
-  hipLaunchKernelGGL((score_select_kernel<T, D, MAXG, KPT>), grid, dim3(kNT), 0, stream, a)
-#define RESA_SS_KPT(MAXG)                              \
-  do {                                                 \
-    if (cand_max <= 8 * kNT) RESA_SS_LAUNCH(MAXG, 8);   \
-    else if (cand_max <= 16 * kNT) RESA_SS_LAUNCH(MAXG, 16); \
-    else if (cand_max <= 32 * kNT) RESA_SS_LAUNCH(MAXG, 32); \
-    else RESA_SS_LAUNCH(MAXG, 0);                      \
-  } while (0)
-  if (a.G <= 8) RESA_SS_KPT(8);
-  else RESA_SS_KPT(16);
-#undef RESA_SS_KPT
-#undef RESA_SS_LAUNCH
+hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
+  constexpr int VPL = ChunkLoad<T>::kVals;
+  constexpr int CH = 2 * D / VPL;
+  // heads per workgroup: all of them while one block of all heads takes at
+  // most kScoreThreads threads
+  int HW = a.H;
+  while (HW > 1 && CH * HW > kScoreThreads) HW = (HW + 1) / 2;
+  const int unit = CH * HW;  // threads per block of all the group's heads
+  int m = 1;
+  while ((unit * m) % 64 != 0) ++m;
+  while (unit * m * 2 <= kScoreThreads && m * 2 * kScoreUnroll <= 64) m *= 2;
+  const int threads = unit * m;  // <= kScoreThreads
+  const int bpi = m;
+  const int blocks_per_wg = bpi * kScoreUnroll;  // <= 64: one table entry per lane
+  const int wgs = (a.max_blocks + blocks_per_wg - 1) / blocks_per_wg;
+  const size_t lds = (size_t)HW * 2 * D * sizeof(float);
+  dim3 grid((unsigned)(wgs + (a.refresh_tail ? 1 : 0)), (unsigned)a.R, (unsigned)((a.H + HW - 1) / HW));
+#define RESA_SCORE_LAUNCH(MODE, MAXG)                                                                        \
+  hipLaunchKernelGGL((score_kernel<T, D, MODE, MAXG>), grid, dim3(threads), lds, stream,                     \
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.desc_pool), a.table, a.seq_lens, a.keys, \
+                     a.scores, a.H, HW, a.G, a.max_blocks, a.num_pool_blocks, static_cast<const T*>(a.k_pool), \
+                     static_cast<T*>(const_cast<void*>(a.desc_pool)), wgs, a.key_stride)
+  if (a.G <= 8) {
+    if (a.mode == 0) RESA_SCORE_LAUNCH(0, 8);
+    else RESA_SCORE_LAUNCH(1, 8);
+  } else {
+    if (a.mode == 0) RESA_SCORE_LAUNCH(0, 16);
+    else RESA_SCORE_LAUNCH(1, 16);
+  }
+#undef RESA_SCORE_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const ScoreArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)a.H, (unsigned)a.R);
+  const long long cand_max = a.key_stride;
+#define RESA_SELECT_LAUNCH(KPT)                                                                              \
+  hipLaunchKernelGGL((select_kernel<KPT>), grid, dim3(kSelectThreads), 0, stream, a.keys, a.seq_lens, a.sel_idx, \
+                     a.sel_cnt, a.H, a.max_blocks, a.max_sel, a.budget_num, a.budget_den, a.min_blocks,      \
+                     a.local_blocks, a.key_stride)
+  if (cand_max <= 8LL * kSelectThreads) RESA_SELECT_LAUNCH(8);
+  else if (cand_max <= 16LL * kSelectThreads) RESA_SELECT_LAUNCH(16);
+  else if (cand_max <= 32LL * kSelectThreads) RESA_SELECT_LAUNCH(32);
+  else RESA_SELECT_LAUNCH(0);
+#undef RESA_SELECT_LAUNCH
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t score_select_sync_bytes(int R, int H) { return (size_t)R * H * kSyncWords * sizeof(uint32_t); }
-size_t score_select_range_bytes(int R, int H, int max_blocks) {
-  return (size_t)R * H * 2 * max_slices(max_blocks) * sizeof(uint32_t);
-}
-
 hipError_t launch_score_select(const ScoreArgs& a, hipStream_t stream) {
-  if (a.dtype == 0) return a.D == 128 ? launch_t<bf16_t, 128>(a, stream) : launch_t<bf16_t, 64>(a, stream);
-  return a.D == 128 ? launch_t<float, 128>(a, stream) : launch_t<float, 64>(a, stream);
+  hipError_t e;
+  if (a.dtype == 0)
+    e = a.D == 128 ? launch_scores_t<bf16_t, 128>(a, stream) : launch_scores_t<bf16_t, 64>(a, stream);
+  else
+    e = a.D == 128 ? launch_scores_t<float, 128>(a, stream) : launch_scores_t<float, 64>(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_select(a, stream);
 }
 
 }  // namespace resa

@@ -140,11 +140,13 @@ int32_t resa_selection_count(const resa_config* cfg, int32_t num_blocks);
  * `max_blocks` blocks; `max_sel` is the sel_idx row capacity (sparse ops) and
  * `chunk` the rectification window (rectify).  Returns 0 on invalid arguments.
  * Calls that share a workspace must be ordered on one stream.
- * Initialisation: the workspaces of RESA_OP_SCORE_SELECT and
- * RESA_OP_SPARSE_STEP hold counters that workgroups of one launch use to hand
- * work to each other; they must be all zero when the workspace is first
- * used (allocate it zeroed), and every call leaves them zero again.  The
- * other workspaces need no initialisation. */
+ * Initialisation: the workspace of RESA_OP_SPARSE_STEP holds counters that
+ * workgroups of one launch use to hand work to each other; they must be all
+ * zero when the workspace is first used (allocate it zeroed), and every call
+ * leaves them zero again.  Their place depends on the call's sizes, so a
+ * step workspace reused with a different num_requests, max_blocks or
+ * max_sel must be zeroed again first.  The other workspaces need no
+ * initialisation. */
 size_t resa_workspace_bytes(const resa_config* cfg, int32_t op, int32_t num_requests,
                             int32_t max_blocks, int32_t max_sel, int32_t chunk);
 
@@ -250,10 +252,11 @@ resa_status resa_sparse_step(const resa_config* cfg, const resa_paged_kv* kv, in
  * A call whose workspace (resa_workspace_bytes(cfg, RESA_OP_SPARSE_DECODE,
  * num_requests, kv->max_blocks, max_sel, 0)) exceeds that size returns
  * RESA_ERR_WORKSPACE and enqueues nothing.  All calls on one GPU share its
- * array and it keeps the last call's contents (every call leaves the words
- * that must start at zero at zero): calls that overlap on one GPU (on
- * different streams, or from several threads) race and must be ordered by
- * the caller.  A failed lookup of the array returns RESA_ERR_LAUNCH.
+ * array and it keeps the last call's contents (the decode writes every word
+ * it reads first, so nothing in it needs clearing): calls that overlap on
+ * one GPU (on different streams, or from several threads) race and must be
+ * ordered by the caller.  A failed lookup of the array returns
+ * RESA_ERR_LAUNCH.
  */
 #define RESA_NOALLOC_SCRATCH_BYTES (8u << 20)
 resa_status resa_sparse_decode_noalloc(const resa_config* cfg, const resa_paged_kv* kv,
