@@ -245,13 +245,21 @@ template <typename T, int D>
 hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
   constexpr int VPL = ChunkLoad<T>::kVals;
   constexpr int CH = 2 * D / VPL;
-  // heads per workgroup: all of them while one block of all heads takes at
-  // most kScoreThreads threads
+  // heads per workgroup: all of them when whole wavefronts of blocks of all
+  // heads fit in kScoreThreads threads, else the largest power of two of
+  // heads whose blocks do
+  auto min_blocks_per_pass = [](int unit) {
+    int m = 1;
+    while ((unit * m) % 64 != 0) ++m;
+    return m;
+  };
   int HW = a.H;
-  while (HW > 1 && CH * HW > kScoreThreads) HW = (HW + 1) / 2;
+  if (CH * HW * min_blocks_per_pass(CH * HW) > kScoreThreads) {
+    HW = 1;
+    while (CH * HW * 2 <= kScoreThreads) HW *= 2;
+  }
   const int unit = CH * HW;  // threads per block of all the group's heads
-  int m = 1;
-  while ((unit * m) % 64 != 0) ++m;
+  int m = min_blocks_per_pass(unit);
   while (unit * m * 2 <= kScoreThreads && m * 2 * kScoreUnroll <= 64) m *= 2;
   const int threads = unit * m;  // <= kScoreThreads
   const int bpi = m;

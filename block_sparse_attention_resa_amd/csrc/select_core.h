@@ -320,7 +320,9 @@ struct Bucket {
 // LDS of the selection by an NT-thread workgroup.
 template <int NT>
 struct SelectLds {
-  uint32_t hist2[2][kBins + 1];  // alternating pass histograms; the last slot takes non-members
+  // alternating pass histograms; slot kBins takes non-members (rows padded
+  // to keep the second one 16-byte aligned for the scan's vector reads)
+  __align__(16) uint32_t hist2[2][kBins + 4];
   WaveSlots<int, NT / 64> scan_slots;
   WaveSlots<uint2, NT / 64> mm_slots;
   __align__(16) uint32_t bucket[kFinishMax + 8];  // read eight at a time
@@ -343,9 +345,9 @@ struct Threshold {
 template <int NT, int KPT>
 __device__ __forceinline__ Threshold select_threshold(SelectLds<NT>& sl, KeyRuns<NT, KPT>& kr, int C, int k,
                                                       uint32_t mn, uint32_t mx, int& scan_use) {
-  constexpr int BPT = kBins / NT;                   // histogram bins per thread in the scan (4 or 8)
+  constexpr int BPT = kBins / NT;                   // histogram bins per thread in the scan (2, 4 or 8)
   constexpr bool kKeepBins = KPT > 0 && KPT * NT <= 16 * 1024;  // first-pass bins kept in registers (16 bits each)
-  static_assert(BPT == 4 || BPT == 8, "the scan reads four or eight bins per thread");
+  static_assert(BPT == 2 || BPT == 4 || BPT == 8, "the scan reads two, four or eight bins per thread");
   int mm_use = 0;  // alternating slot sets, identical in every thread
   const int tid = threadIdx.x;
 
@@ -407,21 +409,32 @@ __device__ __forceinline__ Threshold select_threshold(SelectLds<NT>& sl, KeyRuns
     const int rt = NT - 1 - tid;
     uint32_t hb[BPT];
     int c = 0;
+    if constexpr (BPT == 2) {
+      const uint2 h2 = *reinterpret_cast<const uint2*>(&hist[BPT * rt]);
+      hb[0] = h2.x;
+      hb[1] = h2.y;
+      c = (int)(h2.x + h2.y);
+    } else {
 #pragma unroll
-    for (int e = 0; e < BPT; e += 4) {
-      const uint4 h4 = *reinterpret_cast<const uint4*>(&hist[BPT * rt + e]);
-      hb[e] = h4.x;
-      hb[e + 1] = h4.y;
-      hb[e + 2] = h4.z;
-      hb[e + 3] = h4.w;
-      c += (int)(h4.x + h4.y + h4.z + h4.w);
+      for (int e = 0; e < BPT; e += 4) {
+        const uint4 h4 = *reinterpret_cast<const uint4*>(&hist[BPT * rt + e]);
+        hb[e] = h4.x;
+        hb[e + 1] = h4.y;
+        hb[e + 2] = h4.z;
+        hb[e + 3] = h4.w;
+        c += (int)(h4.x + h4.y + h4.z + h4.w);
+      }
     }
     int tot;
     const int above0 = block_exclusive_scan<NT>(c, sl.scan_slots, scan_use, tot);
     int* bc = sl.bc2[npass & 1];
     // this pass's histogram is read; clear it for the pass after next
+    if constexpr (BPT == 2) {
+      *reinterpret_cast<uint2*>(&hist[BPT * rt]) = make_uint2(0u, 0u);
+    } else {
 #pragma unroll
-    for (int e = 0; e < BPT; e += 4) *reinterpret_cast<uint4*>(&hist[BPT * rt + e]) = make_uint4(0u, 0u, 0u, 0u);
+      for (int e = 0; e < BPT; e += 4) *reinterpret_cast<uint4*>(&hist[BPT * rt + e]) = make_uint4(0u, 0u, 0u, 0u);
+    }
     if (tid == 0) hist[kBins] = 0u;
     if (above0 < remaining && above0 + c >= remaining) {
       int above = above0;
@@ -474,16 +487,22 @@ __device__ __forceinline__ Threshold select_threshold(SelectLds<NT>& sl, KeyRuns
       } else {
         RESA_FOR_KEYS({ mem |= (in && bk.has(kr.key(j)) ? 1u : 0u) << j; });
       }
-      // slots by a scan of the per-thread counts (same-address LDS atomics
-      // would serialize)
-      int n_mem;
-      int pos = block_exclusive_scan<NT>(__popc(mem), sl.scan_slots, scan_use, n_mem);
-      if (mem != 0u) {
+      // Slots: one LDS atomic per wavefront that holds members (a lane per
+      // member would serialise on the one counter); each lane's members
+      // follow those of the lanes before it.  Wavefronts without a member,
+      // and rounds without one in the wavefront, are skipped as a whole.
+      if (__ballot(mem != 0u)) {
+        const int cnt = __popc(mem);
+        const int incl = wave_incl_sum(cnt);
+        int base = 0;
+        if ((tid & 63) == 63) base = atomicAdd(&sl.packed, incl);
+        int pos = __builtin_amdgcn_readlane(base, 63) + incl - cnt;
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
-          if ((mem >> j) & 1u) {
-            if (pos < kFinishMax) sl.bucket[pos] = kr.key(j);
-            ++pos;
+          const bool b = (mem >> j) & 1u;
+          if (__ballot(b)) {
+            if (b && pos < kFinishMax) sl.bucket[pos] = kr.key(j);
+            pos += b ? 1 : 0;
           }
         }
       }

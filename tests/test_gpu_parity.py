@@ -25,6 +25,8 @@ CASES = {
     "f32_d128_h2_g5": dict(spec=WORKLOADS["tiny_f32_ctx2k"].with_(num_kv_heads=2, group_size=5,
                                                                   head_dim=128, seq_lens=(1000,))),
     "bf16_g16_L3000": dict(spec=BF.with_(num_kv_heads=1, group_size=16, seq_lens=(3000,))),
+    # 17 KV heads: more heads than one scoring workgroup holds (two head groups)
+    "bf16_h17_g2": dict(spec=BF.with_(num_kv_heads=17, group_size=2, seq_lens=(1500,), outlier_channels=4)),
     "bf16_mean_pool": dict(spec=BF.with_(seq_lens=(4000,)), score_mode=resa.RESA_SCORE_MEAN_POOL),
     "bf16_budget3_local3": dict(spec=BF.with_(seq_lens=(2000,), budget_num=3, budget_den=10,
                                               local_blocks=3, min_blocks=4)),
