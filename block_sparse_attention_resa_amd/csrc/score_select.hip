@@ -30,6 +30,7 @@ namespace {
 constexpr int kScoreUnroll = 4;     // blocks per thread (passes) in the scoring kernel
 constexpr int kScoreThreads = 256;  // threads of a scoring workgroup, at most
 constexpr int kSelectThreads = 1024;
+constexpr int kSelectSmall = 512;  // threads of the selection of rows of up to 4096 keys
 
 template <typename T, int D, int MODE, int MAXG>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
@@ -184,14 +185,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   }
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(const uint32_t* __restrict__ keys,
-                                                               const int32_t* __restrict__ seq_lens,
-                                                               int32_t* __restrict__ sel_idx,
-                                                               int32_t* __restrict__ sel_cnt, int H, int max_blocks,
-                                                               int max_sel, int budget_num, int budget_den,
-                                                               int min_blocks, int local_blocks, int key_stride) {
-  constexpr int NT = kSelectThreads;
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__ keys,
+                                                    const int32_t* __restrict__ seq_lens,
+                                                    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
+                                                    int H, int max_blocks, int max_sel, int budget_num,
+                                                    int budget_den, int min_blocks, int local_blocks,
+                                                    int key_stride) {
   __shared__ SelectLds<NT> sl;
   const int i = blockIdx.x;
   const int r = blockIdx.y;
@@ -286,14 +286,18 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
 hipError_t launch_select(const ScoreArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)a.H, (unsigned)a.R);
   const long long cand_max = a.key_stride;
-#define RESA_SELECT_LAUNCH(KPT)                                                                              \
-  hipLaunchKernelGGL((select_kernel<KPT>), grid, dim3(kSelectThreads), 0, stream, a.keys, a.seq_lens, a.sel_idx, \
-                     a.sel_cnt, a.H, a.max_blocks, a.max_sel, a.budget_num, a.budget_den, a.min_blocks,      \
-                     a.local_blocks, a.key_stride)
-  if (cand_max <= 8LL * kSelectThreads) RESA_SELECT_LAUNCH(8);
-  else if (cand_max <= 16LL * kSelectThreads) RESA_SELECT_LAUNCH(16);
-  else if (cand_max <= 32LL * kSelectThreads) RESA_SELECT_LAUNCH(32);
-  else RESA_SELECT_LAUNCH(0);
+#define RESA_SELECT_LAUNCH(NT, KPT)                                                                           \
+  hipLaunchKernelGGL((select_kernel<NT, KPT>), grid, dim3(NT), 0, stream, a.keys, a.seq_lens, a.sel_idx, a.sel_cnt, \
+                     a.H, a.max_blocks, a.max_sel, a.budget_num, a.budget_den, a.min_blocks, a.local_blocks,   \
+                     a.key_stride)
+  // rows of up to 4096 keys: half the threads (every barrier waits for half
+  // the wavefronts)
+  if (cand_max <= 4LL * kSelectSmall) RESA_SELECT_LAUNCH(kSelectSmall, 4);
+  else if (cand_max <= 8LL * kSelectSmall) RESA_SELECT_LAUNCH(kSelectSmall, 8);
+  else if (cand_max <= 8LL * kSelectThreads) RESA_SELECT_LAUNCH(kSelectThreads, 8);
+  else if (cand_max <= 16LL * kSelectThreads) RESA_SELECT_LAUNCH(kSelectThreads, 16);
+  else if (cand_max <= 32LL * kSelectThreads) RESA_SELECT_LAUNCH(kSelectThreads, 32);
+  else RESA_SELECT_LAUNCH(kSelectThreads, 0);
 #undef RESA_SELECT_LAUNCH
   return hipGetLastError();
 }
