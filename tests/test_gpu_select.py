@@ -111,7 +111,9 @@ def test_select_distributions_16k(dist):
     run_case(dist, 16384, seed=11)
 
 
-@pytest.mark.parametrize("M", [20, 200, 300, 5000, 30000, 40000])
+# sizes on both sides of every change of the selection's thread count and
+# keys per thread (rows of up to 2048, 4096, 8192, 16384 and 32768 keys)
+@pytest.mark.parametrize("M", [20, 200, 300, 2048, 2052, 4096, 4100, 5000, 8192, 8196, 30000, 40000])
 @pytest.mark.parametrize("dist", ["normal", "few_levels", "huge_outlier"])
 def test_select_sizes(dist, M):
     run_case(dist, M, seed=M)
