@@ -168,9 +168,12 @@ struct KeyRuns {
   uint32_t in_mask;  // KPT > 0: bit j set when this thread's key j is a candidate
   bool full;         // KPT > 0, uniform over the wavefront: every key of every lane is a candidate
   bool any;          // KPT > 0, uniform over the wavefront: some lane holds a candidate
-  // The keys were written by other workgroups of the same launch: they are
-  // read at device scope (16-byte buffer loads with the device-scope cache
-  // policy), never from a line an earlier read left in a nearer cache.
+  // SAME_LAUNCH: the keys were written by other workgroups of the same
+  // launch, so they are read at device scope (16-byte buffer loads with the
+  // device-scope cache policy), never from a line an earlier read left in a
+  // nearer cache.  Keys written by an earlier launch are read with plain
+  // 16-byte loads: the launch boundary has made them visible.
+  template <bool SAME_LAUNCH>
   __device__ void prefetch(const uint32_t* kr, int row_stride) {
     row = kr;
     if constexpr (KPT > 0) {
@@ -178,7 +181,8 @@ struct KeyRuns {
 #pragma unroll
       for (int v = 0; v < KPT / 4; ++v) {
         const int idx = (int)threadIdx.x * (KPT / 4) + v;
-        const uint4 x = load16_agent(kr, row_stride, idx < last ? idx : last);
+        const int q = idx < last ? idx : last;
+        const uint4 x = SAME_LAUNCH ? load16_agent(kr, row_stride, q) : *reinterpret_cast<const uint4*>(kr + 4 * q);
         reg[4 * v] = x.x;
         reg[4 * v + 1] = x.y;
         reg[4 * v + 2] = x.z;

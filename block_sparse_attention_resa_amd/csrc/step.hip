@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(const StepArgs a) {
       } else {
         // no usable band: every candidate of the row
         KeyRuns<NT, KPT> kr;
-        kr.prefetch(key_row, a.key_stride);
+        kr.template prefetch<true>(key_row, a.key_stride);
         kr.set_count(ri.C);
         const Threshold th = select_threshold<NT, KPT>(sl, kr, ri.C, ri.k, mn, mx, sel_use);
         thr = th.thr;
