@@ -371,8 +371,13 @@ def main(argv=None):
     t_tail = per_call(tail_refresh)
     t_sel = per_call(score_select)
     t_dec = per_call(sparse_decode)
+    # the same layer-step through the one-call entry point (at this row length
+    # it runs the same kernels as the two calls)
+    ws_step = resa.alloc_workspace(cfg, resa.OP_SPARSE_STEP, 1, mb, ms)
+    t_step_call = per_call(lambda st: resa.sparse_step(cfg, st["kv"], st["q"], st["sel_idx"], st["sel_cnt"],
+                                                       st["out"], ws_step, refresh_tail=True))
     log(f"breakdown us: tail-descriptor call {t_tail:.2f}  score+select (with tail refresh) {t_sel:.2f}  "
-        f"sparse decode {t_dec:.2f}")
+        f"sparse decode {t_dec:.2f}  resa_sparse_step {t_step_call:.2f}")
 
     # ---------------------------------------------------------------- dense
     g_dense = capture(dense_step)
@@ -498,7 +503,8 @@ def main(argv=None):
         "speedup_vs_dense": round(us_dense / us_layer, 3),
         "dense_hbm_gbps": round(dense_bytes / (us_dense * 1e-6) / 1e9, 1),
         "breakdown_us": {"score_select_with_tail_refresh": round(t_sel, 2), "sparse_decode": round(t_dec, 2),
-                         "standalone_tail_descriptor_call": round(t_tail, 2)},
+                         "standalone_tail_descriptor_call": round(t_tail, 2),
+                         "sparse_step_call": round(t_step_call, 2)},
         "rectify_us_per_layer": round(t_rect, 1),
         "rectify_window": RECT_CHUNK,
         "rectify_tflops": round(rect_flops / (t_rect * 1e-6) / 1e12, 2),
@@ -538,8 +544,9 @@ SWEEP_BUDGETS = ((1, 50), (1, 20), (1, 10), (1, 5))
 
 
 def sweep(args):
-    """Per layer-step time of the sparse path (score/select with the tail
-    refresh + sparse decode) for contexts 16K / 64K / 256K, budgets
+    """Per layer-step time of the sparse path (resa_sparse_step with the tail
+    refresh, and beside it the two calls resa_score_select +
+    resa_sparse_decode) for contexts 16K / 64K / 256K, budgets
     2 / 5 / 10 / 20 % and both scoring modes at 10 %, next to the dense decode
     and the rectification of a 32-token window.  Every figure is a HIP-graph
     replay over enough layer caches that one replay touches more than 1 GiB
@@ -623,6 +630,7 @@ def sweep(args):
                    "out": torch.empty((1, H * g, d), device="cuda"), **c} for c in caches]
             ws_s = resa.alloc_workspace(cfg, resa.OP_SCORE_SELECT, 1, mb, ms)
             ws_d = resa.alloc_workspace(cfg, resa.OP_SPARSE_DECODE, 1, mb, ms)
+            ws_st = resa.alloc_workspace(cfg, resa.OP_SPARSE_STEP, 1, mb, ms)
 
             def sel(c):
                 resa.score_select(cfg, c["kv"], c["q"], c["sel"], c["cnt"], ws_s, refresh_tail=True)
@@ -631,6 +639,10 @@ def sweep(args):
                 resa.sparse_decode(cfg, c["kv"], c["q"], c["sel"], c["cnt"], c["out"], ws_d)
 
             gs = graph_of(lambda: [(sel(c), dec(c)) for c in st])
+            us_two = replay_us(gs, nl)
+            del gs
+            gs = graph_of(lambda: [resa.sparse_step(cfg, c["kv"], c["q"], c["sel"], c["cnt"], c["out"], ws_st,
+                                                    refresh_tail=True) for c in st])
             us_step = replay_us(gs, nl)
             del gs
             gsel = graph_of(lambda: [sel(c) for c in st])
@@ -641,7 +653,8 @@ def sweep(args):
             desc_b = H * ((L + 15) // 16) * 2 * d * 2
             kv_b = H * ((n_sel - 1) * 16 + (L - ((L + 15) // 16 - 1) * 16)) * 2 * d * 2
             rows.append({"ctx": L, "budget": f"{num}/{den_}", "mode": "sum" if mode == 0 else "mean-pool",
-                         "n_sel": n_sel, "us_step": us_step, "us_score_select": t_sel, "us_decode": t_dec,
+                         "n_sel": n_sel, "us_step": us_step, "us_two": us_two, "us_score_select": t_sel,
+                         "us_decode": t_dec,
                          "us_dense": us_dense, "us_rectify_f32": us_rect,
                          "gbps": (desc_b + kv_b) / (us_step * 1e-6) / 1e9,
                          "speedup": us_dense / us_step,
@@ -650,11 +663,11 @@ def sweep(args):
         del caches, den
         torch.cuda.empty_cache()
 
-    print("| ctx | budget | scoring | blocks | us/layer-step | score+select us | sparse decode us | GB/s (alg.) "
-          "| dense us | x dense | rectify f=32 us | x dense incl. rectify/32 |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    print("| ctx | budget | scoring | blocks | us/layer-step | two calls us | score+select us | sparse decode us "
+          "| GB/s (alg.) | dense us | x dense | rectify f=32 us | x dense incl. rectify/32 |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for r in rows:
-        print(f"| {r['ctx']} | {r['budget']} | {r['mode']} | {r['n_sel']} | {r['us_step']:.1f} | "
+        print(f"| {r['ctx']} | {r['budget']} | {r['mode']} | {r['n_sel']} | {r['us_step']:.1f} | {r['us_two']:.1f} | "
               f"{r['us_score_select']:.1f} | {r['us_decode']:.1f} | {r['gbps']:.0f} | {r['us_dense']:.1f} | "
               f"{r['speedup']:.2f} | {r['us_rectify_f32']:.0f} | {r['cycle_speedup']:.2f} |")
     return 0
@@ -772,8 +785,9 @@ WORKLOAD_TABLE = ("qwen7b_ctx32k_b1", "qwen7b_ragged_b8", "qwen7b_ctx131k_b4_rec
 
 def workloads(args):
     """The bf16 workloads of the measured configurations, each at its own
-    batch and context: per layer-step time of the sparse step (score/select
-    with the tail refresh + sparse decode, all requests of one layer), decode
+    batch and context: per layer-step time of the sparse step
+    (resa_sparse_step with the tail refresh, all requests of one layer; and
+    beside it the two calls resa_score_select + resa_sparse_decode), decode
     tokens/s over 28 layers (attention only), algorithmic GB/s and its
     fraction of 8 TB/s, the dense decode and the speedup, and the
     rectification of the workload's window (the rectify workload's f, else
@@ -839,11 +853,18 @@ def workloads(args):
         ws_s = resa.alloc_workspace(cfg, resa.OP_SCORE_SELECT, R, mb, ms)
         ws_d = resa.alloc_workspace(cfg, resa.OP_SPARSE_DECODE, R, mb, ms)
         ws_n = resa.alloc_workspace(cfg, resa.OP_DENSE_DECODE, R, mb)
+        ws_st = resa.alloc_workspace(cfg, resa.OP_SPARSE_STEP, R, mb, ms)
 
-        def step(c):
+        def two_calls(c):
             resa.score_select(cfg, c["kv"], c["q"], c["sel"], c["cnt"], ws_s, refresh_tail=True)
             resa.sparse_decode(cfg, c["kv"], c["q"], c["sel"], c["cnt"], c["out"], ws_d)
 
+        def step(c):
+            resa.sparse_step(cfg, c["kv"], c["q"], c["sel"], c["cnt"], c["out"], ws_st, refresh_tail=True)
+
+        gs = graph_of(lambda: [two_calls(c) for c in st])
+        us_two = replay_us(gs, nl, 20)
+        del gs
         gs = graph_of(lambda: [step(c) for c in st])
         us_step = replay_us(gs, nl, 20)
         del gs
@@ -871,17 +892,18 @@ def workloads(args):
         gbps = alg / (us_step * 1e-6) / 1e9
         rows.append({"name": name, "R": R, "ctx": f"{min(lens)}" if min(lens) == max(lens) else f"{min(lens)}-{max(lens)}",
                      "nsel": f"{min(nsel)}" if min(nsel) == max(nsel) else f"{min(nsel)}-{max(nsel)}",
-                     "us": us_step, "tok": R / (28 * us_step * 1e-6), "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS,
+                     "us": us_step, "two": us_two, "tok": R / (28 * us_step * 1e-6), "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS,
                      "dense": us_dense, "x": us_dense / us_step, "f": f, "rect": us_rect,
                      "tflops": flops / (us_rect * 1e-6) / 1e12})
         del st, caches, qc, kn, vn, rout
         torch.cuda.empty_cache()
 
-    print("| workload | requests | context | blocks/head | us/layer-step | tokens/s (28 layers) | GB/s (alg.) "
-          "| of 8 TB/s | dense us | x dense | rectify f | rectify us | rectify TFLOP/s | of 2.5 PFLOP/s |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+    print("| workload | requests | context | blocks/head | us/layer-step | two calls us | tokens/s (28 layers) "
+          "| GB/s (alg.) | of 8 TB/s | dense us | x dense | rectify f | rectify us | rectify TFLOP/s "
+          "| of 2.5 PFLOP/s |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for r in rows:
-        print(f"| {r['name']} | {r['R']} | {r['ctx']} | {r['nsel']} | {r['us']:.1f} | {r['tok']:.0f} | "
+        print(f"| {r['name']} | {r['R']} | {r['ctx']} | {r['nsel']} | {r['us']:.1f} | {r['two']:.1f} | {r['tok']:.0f} | "
               f"{r['gbps']:.0f} | {r['frac'] * 100:.1f} % | {r['dense']:.1f} | {r['x']:.2f} | {r['f']} | "
               f"{r['rect']:.0f} | {r['tflops']:.0f} | {r['tflops'] / 2500 * 100:.1f} % |")
     return 0

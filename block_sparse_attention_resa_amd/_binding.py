@@ -272,7 +272,7 @@ def sparse_decode(cfg: Config, kv: PagedKV, q: torch.Tensor, sel_idx: torch.Tens
 
 def sparse_step(cfg: Config, kv: PagedKV, q: torch.Tensor, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
                 out: torch.Tensor, workspace: torch.Tensor, refresh_tail: bool = False) -> None:
-    """resa_score_select + resa_sparse_decode as one launch (workspace of OP_SPARSE_STEP, zeroed)."""
+    """resa_score_select + resa_sparse_decode in one launch fewer (workspace of OP_SPARSE_STEP)."""
     _check_cache(cfg, kv)
     R, H, G, d = kv.num_requests, cfg.num_kv_heads, cfg.group_size, cfg.head_dim
     _need(q, "q", cfg.torch_dtype, (R, H * G, d))

@@ -126,13 +126,9 @@ size_t workspace_bytes(const resa_config* c, int op, int R, int max_blocks, int 
       const int S = splits_for(c, op, R, max_blocks, max_sel, chunk);
       return partial_bytes(c, R, S, (long long)chunk * c->group_size);
     }
-    case RESA_OP_SPARSE_STEP: {
-      size_t parts[kStepParts];
-      step_workspace_parts(c->dtype, c->head_dim, R, c->num_kv_heads, c->group_size, max_blocks, max_sel, parts);
-      size_t total = 0;
-      for (size_t b : parts) total += align_up(b);
-      return total;
-    }
+    case RESA_OP_SPARSE_STEP:  // the score keys, then the sparse decode's partials
+      return workspace_bytes(c, RESA_OP_SCORE_SELECT, R, max_blocks, max_sel, 0) +
+             workspace_bytes(c, RESA_OP_SPARSE_DECODE, R, max_blocks, max_sel, 0);
     default:
       return 0;
   }
@@ -384,64 +380,60 @@ resa_status resa_sparse_step(const resa_config* cfg, const resa_paged_kv* kv, in
   if (num_requests == 0) return RESA_OK;
   const size_t need = workspace_bytes(cfg, RESA_OP_SPARSE_STEP, num_requests, kv->max_blocks, max_sel, 0);
   if (!ws || ws_bytes < need || !aligned16(ws)) return RESA_ERR_WORKSPACE;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    return RESA_ERR_LAUNCH;
-  StepArgs a{};
-  a.q = q;
-  a.k_pool = kv->k_pool;
-  a.v_pool = kv->v_pool;
-  a.desc_pool = kv->desc_pool;
-  a.table = kv->block_table;
-  a.seq_lens = kv->seq_lens;
-  a.refresh_tail = refresh_tail != 0;
-  a.sel_idx = sel_idx;
-  a.sel_cnt = sel_cnt;
-  a.out = out;
-  size_t parts[kStepParts];
-  step_workspace_parts(cfg->dtype, cfg->head_dim, num_requests, cfg->num_kv_heads, cfg->group_size, kv->max_blocks,
-                       max_sel, parts);
-  char* base = static_cast<char*>(ws);
-  size_t off = 0;
-  void* ptr[kStepParts];
-  for (int k = 0; k < kStepParts; ++k) {
-    ptr[k] = base + off;
-    off += align_up(parts[k]);
-  }
-  a.flags = static_cast<uint32_t*>(ptr[0]);
-  a.stats = static_cast<uint32_t*>(ptr[1]);
-  a.cnts = static_cast<uint32_t*>(ptr[2]);
-  a.keys = static_cast<uint32_t*>(ptr[3]);
-  a.band = static_cast<uint32_t*>(ptr[4]);
-  a.part_o = static_cast<float*>(ptr[5]);
-  a.part_ml = static_cast<float*>(ptr[6]);
-  a.R = num_requests;
-  a.H = cfg->num_kv_heads;
-  a.G = cfg->group_size;
-  a.D = cfg->head_dim;
-  a.dtype = cfg->dtype;
-  a.max_blocks = kv->max_blocks;
-  a.num_pool_blocks = kv->num_pool_blocks;
-  a.mode = cfg->score_mode;
-  a.key_stride = key_stride_for(kv->max_blocks);
-  a.band_stride = step_band_stride(cfg->dtype, cfg->head_dim, num_requests, cfg->num_kv_heads, kv->max_blocks);
-  a.max_sel = max_sel;
-  a.budget_num = cfg->budget_num;
-  a.budget_den = cfg->budget_den;
-  a.min_blocks = cfg->min_blocks;
-  a.local_blocks = cfg->local_blocks;
-  a.scale_log2 = scale_log2(cfg);
-  step_geometry(cfg->dtype, cfg->head_dim, num_requests, cfg->num_kv_heads, kv->max_blocks, &a.unroll, &a.nslices);
-  // One workgroup per compute unit at most: every workgroup of the grid is
-  // resident at once, and the slices of a row fit in one sweep of the grid,
-  // which the waits between the slices of a row rely on.
-  const long long units = (long long)num_requests * cfg->num_kv_heads * a.nslices;
-  if (units > 0x7fffffffLL) return RESA_ERR_UNSUPPORTED;
-  a.grid = (int)(units < cus ? units : cus);
-  if (a.nslices > a.grid) return RESA_ERR_UNSUPPORTED;
+  const size_t key_bytes = workspace_bytes(cfg, RESA_OP_SCORE_SELECT, num_requests, kv->max_blocks, max_sel, 0);
+  char* parts = static_cast<char*>(ws) + key_bytes;  // the decode's partials follow the keys
+  const int S = splits_for(cfg, RESA_OP_SPARSE_DECODE, num_requests, kv->max_blocks, max_sel, 0);
+  const size_t rows = (size_t)num_requests * cfg->num_kv_heads * S * cfg->group_size;
+
+  ScoreArgs sa{};
+  sa.q = q;
+  sa.desc_pool = kv->desc_pool;
+  sa.k_pool = kv->k_pool;
+  sa.refresh_tail = refresh_tail != 0;
+  sa.table = kv->block_table;
+  sa.seq_lens = kv->seq_lens;
+  sa.keys = static_cast<uint32_t*>(ws);
+  sa.scores = nullptr;
+  sa.sel_idx = sel_idx;
+  sa.sel_cnt = sel_cnt;
+  sa.R = num_requests;
+  sa.H = cfg->num_kv_heads;
+  sa.G = cfg->group_size;
+  sa.D = cfg->head_dim;
+  sa.dtype = cfg->dtype;
+  sa.max_blocks = kv->max_blocks;
+  sa.num_pool_blocks = kv->num_pool_blocks;
+  sa.mode = cfg->score_mode;
+  sa.key_stride = key_stride_for(kv->max_blocks);
+  sa.max_sel = max_sel;
+  sa.budget_num = cfg->budget_num;
+  sa.budget_den = cfg->budget_den;
+  sa.min_blocks = cfg->min_blocks;
+  sa.local_blocks = cfg->local_blocks;
+
+  DecodeArgs da{};
+  da.q = q;
+  da.k_pool = kv->k_pool;
+  da.v_pool = kv->v_pool;
+  da.table = kv->block_table;
+  da.seq_lens = kv->seq_lens;
+  da.sel_idx = sel_idx;
+  da.sel_cnt = sel_cnt;
+  da.max_sel = max_sel;
+  da.out = out;
+  da.part_o = reinterpret_cast<float*>(parts);
+  da.part_ml = reinterpret_cast<float*>(parts + align_up(rows * cfg->head_dim * sizeof(float)));
+  da.R = num_requests;
+  da.H = cfg->num_kv_heads;
+  da.G = cfg->group_size;
+  da.D = cfg->head_dim;
+  da.dtype = cfg->dtype;
+  da.max_blocks = kv->max_blocks;
+  da.num_pool_blocks = kv->num_pool_blocks;
+  da.splits = S;
+  da.scale_log2 = scale_log2(cfg);
   (void)hipGetLastError();
-  return from_hip(launch_step(a, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_step(sa, da, static_cast<hipStream_t>(stream)));
 }
 
 resa_status resa_dense_decode(const resa_config* cfg, const resa_paged_kv* kv, int32_t num_requests, const void* q,

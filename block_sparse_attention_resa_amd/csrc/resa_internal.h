@@ -69,7 +69,7 @@ struct DescArgs {
 };
 hipError_t launch_descriptors(const DescArgs& a, hipStream_t stream);
 
-// Scoring and selection of resa_score_select (one launch).
+// Scoring and selection of resa_score_select.
 struct ScoreArgs {
   const void* q;
   const void* desc_pool;  // also written (tail block) when refresh_tail
@@ -92,41 +92,6 @@ hipError_t launch_score_select(const ScoreArgs& a, hipStream_t stream);
 // 16-byte aligned and the selection can read its keys with 16-byte loads.
 inline int key_stride_for(int max_blocks) { return (max_blocks + 3) & ~3; }
 
-// One decode step of one layer (resa_sparse_step) in one persistent launch.
-struct StepArgs {
-  const void* q;
-  const void* k_pool;
-  const void* v_pool;
-  void* desc_pool;  // read; the tail block's descriptor written when refresh_tail
-  const int32_t* table;
-  const int32_t* seq_lens;
-  int32_t refresh_tail;
-  int32_t* sel_idx;
-  int32_t* sel_cnt;
-  float* out;
-  uint32_t* flags;  // [R][H][5][32] counters and state words, zero between calls
-  uint32_t* stats;  // [R][H][W][4] per-slice key statistics
-  uint32_t* cnts;   // [R][H][W][4] per-slice counts
-  uint32_t* keys;   // [R][H][key_stride]
-  uint32_t* band;   // [R][H][band_stride][2] band keys and their block ids, by slice
-  float* part_o;    // [R][H][W][G][D]
-  float* part_ml;   // [R][H][W][G][2]
-  int32_t R, H, G, D, dtype, max_blocks, num_pool_blocks, mode, key_stride, band_stride, max_sel;
-  int32_t budget_num, budget_den, min_blocks, local_blocks;
-  float scale_log2;
-  int32_t unroll, nslices, grid;  // from step_geometry / the launcher
-};
-// Slices of the step: passes per slice (unroll) and slices per (request,
-// KV head).
-void step_geometry(int dtype, int D, int R, int H, int max_blocks, int* unroll, int* nslices);
-// Band entries per (request, KV head): slices times blocks per slice.
-int step_band_stride(int dtype, int D, int R, int H, int max_blocks);
-constexpr int kStepParts = 7;
-// Bytes of each workspace part of the step, in the order of StepArgs.
-void step_workspace_parts(int dtype, int D, int R, int H, int G, int max_blocks, int max_sel,
-                          size_t parts[kStepParts]);
-hipError_t launch_step(const StepArgs& a, hipStream_t stream);
-
 struct DecodeArgs {
   const void* q;
   const void* k_pool;
@@ -143,6 +108,19 @@ struct DecodeArgs {
   float scale_log2;  // sm_scale * log2(e)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// The two launches of resa_score_select on their own.
+hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream);
+hipError_t launch_select(const ScoreArgs& a, hipStream_t stream);
+
+// One decode step of one layer (resa_sparse_step): the scoring launch, then
+// the selection fused with the split attention, then the merge of the
+// splits.  `sa` carries the scoring and selection arguments (sel_idx,
+// sel_cnt, keys), `da` the attention's (splits, partials, out).  Whether
+// the fused launch serves these sizes (else the selection launch and the
+// decode launch run in its place):
+bool step_fused(int dtype, int key_stride, int max_sel, int splits);
+hipError_t launch_step(const ScoreArgs& sa, const DecodeArgs& da, hipStream_t stream);
 
 // Log-sum-exp merge of split partials: out row (r, t, i*G + j) from
 // part_o / part_ml rows ((r*H + i)*S + s)*rows_per_head + t*G + j.

@@ -283,6 +283,8 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+}  // namespace
+
 hipError_t launch_select(const ScoreArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)a.H, (unsigned)a.R);
   const long long cand_max = a.key_stride;
@@ -302,14 +304,14 @@ hipError_t launch_select(const ScoreArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-}  // namespace
+hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream) {
+  if (a.dtype == 0)
+    return a.D == 128 ? launch_scores_t<bf16_t, 128>(a, stream) : launch_scores_t<bf16_t, 64>(a, stream);
+  return a.D == 128 ? launch_scores_t<float, 128>(a, stream) : launch_scores_t<float, 64>(a, stream);
+}
 
 hipError_t launch_score_select(const ScoreArgs& a, hipStream_t stream) {
-  hipError_t e;
-  if (a.dtype == 0)
-    e = a.D == 128 ? launch_scores_t<bf16_t, 128>(a, stream) : launch_scores_t<bf16_t, 64>(a, stream);
-  else
-    e = a.D == 128 ? launch_scores_t<float, 128>(a, stream) : launch_scores_t<float, 64>(a, stream);
+  const hipError_t e = launch_scores(a, stream);
   if (e != hipSuccess) return e;
   return launch_select(a, stream);
 }

@@ -595,6 +595,37 @@ __device__ __forceinline__ int cut_position(SelectLds<NT>& sl, KeyRuns<NT, KPT>&
   return *res;
 }
 
+// The keys this thread takes of a row's top-k (register-held keys, KPT > 0):
+// bit j of `take` is set when block KPT t + j is selected, and `pos` is the
+// place of the first of them in the ascending list of the k selected ids
+// (the others follow it in bit order).  Each thread's keys are consecutive
+// blocks, so one scan of the per-thread counts gives every thread its first
+// output position; ties at the threshold are ranked the same way.  Every
+// thread of the workgroup calls it.
+template <int NT, int KPT>
+__device__ __forceinline__ void select_take(SelectLds<NT>& sl, KeyRuns<NT, KPT>& kr, const Threshold& th,
+                                            int& scan_use, uint32_t& take, int& pos) {
+  static_assert(KPT > 0, "register-held keys only");
+  const uint32_t thr = th.thr;
+  const bool ties = th.take_eq < th.n_eq;
+  take = 0;
+  if (!ties) {  // every key at or above the threshold
+    RESA_FOR_KEYS({ take |= (in && kr.key(j) >= thr ? 1u : 0u) << j; });
+  } else {  // of the keys equal to the threshold, the take_eq lowest block ids
+    uint32_t equal = 0;
+    RESA_FOR_KEYS({
+      const uint32_t x = kr.key(j);
+      take |= (in && x > thr ? 1u : 0u) << j;
+      equal |= (in && x == thr ? 1u : 0u) << j;
+    });
+    int n_all;
+    int room = th.take_eq - block_exclusive_scan<NT>(__popc(equal), sl.scan_slots, scan_use, n_all);
+    for (uint32_t m = equal; m != 0u && room > 0; m &= m - 1u, --room) take |= m & (~m + 1u);
+  }
+  int tot;
+  pos = block_exclusive_scan<NT>(__popc(take), sl.scan_slots, scan_use, tot);
+}
+
 // Top-k of the C candidate keys of one row (k in (0, C)) held by `kr`
 // (prefetched, count set), whose range [mn, mx] is known: writes the k
 // selected block ids, ascending, to out.  Expects the two histograms and
@@ -606,35 +637,20 @@ __device__ __forceinline__ void select_top(SelectLds<NT>& sl, KeyRuns<NT, KPT>& 
   int scan_use = 0;
   const int tid = threadIdx.x;
   const Threshold th = select_threshold<NT, KPT>(sl, kr, C, k, mn, mx, scan_use);
-  const uint32_t thr = th.thr;
-  const int take_eq = th.take_eq, n_eq = th.n_eq;
 
-  // Output in ascending block order.  Each thread's keys are consecutive
-  // blocks, so one scan of the per-thread counts gives every thread its first
-  // output position; ties at the threshold are ranked the same way.
-  const bool ties = take_eq < n_eq;
+  // Output in ascending block order.
   if constexpr (KPT > 0) {
-    uint32_t take = 0;
-    if (!ties) {  // every key at or above the threshold
-      RESA_FOR_KEYS({ take |= (in && kr.key(j) >= thr ? 1u : 0u) << j; });
-    } else {  // of the keys equal to the threshold, the take_eq lowest block ids
-      uint32_t equal = 0;
-      RESA_FOR_KEYS({
-        const uint32_t x = kr.key(j);
-        take |= (in && x > thr ? 1u : 0u) << j;
-        equal |= (in && x == thr ? 1u : 0u) << j;
-      });
-      int n_all;
-      int room = take_eq - block_exclusive_scan<NT>(__popc(equal), sl.scan_slots, scan_use, n_all);
-      for (uint32_t m = equal; m != 0u && room > 0; m &= m - 1u, --room) take |= m & (~m + 1u);
-    }
-    int tot;
-    int pos = block_exclusive_scan<NT>(__popc(take), sl.scan_slots, scan_use, tot);
+    uint32_t take;
+    int pos;
+    select_take<NT, KPT>(sl, kr, th, scan_use, take, pos);
     const int first = tid * KPT;
     for (uint32_t m = take; m != 0u; m &= m - 1u, ++pos)
       if (pos < k) out[pos] = first + __builtin_ctz(m);
   } else {
     // Any number of rounds: one block scan per round.
+    const uint32_t thr = th.thr;
+    const int take_eq = th.take_eq;
+    const bool ties = take_eq < th.n_eq;
     const int R = kr.nrounds();
     int base_out = 0, base_eq = 0;
     for (int j = 0; j < R; ++j) {

@@ -16,7 +16,7 @@
  *                           positions' rows, refresh their descriptors, and
  *                           run causal chunk attention over the whole cache
  *   resa_sparse_step        resa_score_select followed by resa_sparse_decode
- *                           as one launch (the decode step of one layer)
+ *                           in one launch fewer (the decode step of one layer)
  *
  * Conventions for every call
  * --------------------------
@@ -139,14 +139,8 @@ int32_t resa_selection_count(const resa_config* cfg, int32_t num_blocks);
 /* Bytes of workspace `op` needs for `num_requests` requests of up to
  * `max_blocks` blocks; `max_sel` is the sel_idx row capacity (sparse ops) and
  * `chunk` the rectification window (rectify).  Returns 0 on invalid arguments.
- * Calls that share a workspace must be ordered on one stream.
- * Initialisation: the workspace of RESA_OP_SPARSE_STEP holds counters that
- * workgroups of one launch use to hand work to each other; they must be all
- * zero when the workspace is first used (allocate it zeroed), and every call
- * leaves them zero again.  Their place depends on the call's sizes, so a
- * step workspace reused with a different num_requests, max_blocks or
- * max_sel must be zeroed again first.  The other workspaces need no
- * initialisation. */
+ * Calls that share a workspace must be ordered on one stream.  No
+ * workspace needs initialisation. */
 size_t resa_workspace_bytes(const resa_config* cfg, int32_t op, int32_t num_requests,
                             int32_t max_blocks, int32_t max_sel, int32_t chunk);
 
@@ -219,21 +213,22 @@ resa_status resa_sparse_decode(const resa_config* cfg, const resa_paged_kv* kv,
  * One decode step of one layer: exactly what resa_score_select(cfg, kv,
  * num_requests, q, refresh_tail, sel_idx, sel_cnt, max_sel, NULL, ...)
  * followed by resa_sparse_decode(cfg, kv, num_requests, q, sel_idx, sel_cnt,
- * max_sel, out, ...) compute - the same sel_idx and sel_cnt, and out within
- * floating-point rounding of the two-call result (the attention is split
- * differently) - in a single persistent launch.  Blocks whose score already
- * proves them selected (a bound from per-slice order statistics, see the
- * kernel source) are attended while the exact selection is still running.
- * The launch keeps at most one workgroup per compute unit and its
- * workgroups wait for each other (bounded waits, each about a second at
- * most); it relies on all of them being resident at once, which holds when
- * no other work occupies the device's compute units during the call.
+ * max_sel, out, ...) compute - the same sel_idx and sel_cnt, and the same out
+ * (the attention is split the same way) - in one launch fewer: the scoring
+ * launch, then one launch in which every split workgroup of a (request, KV
+ * head) finds the row's selection threshold itself from the score keys and
+ * attends over its own share of the selected list, then the merge of the
+ * splits (split execution with a log-sum-exp merge: "Rectified Sparse
+ * Attention" analysis page, §3.4.4; kernel time without CPU overhead: §5).
+ * Rows of more than 8192 blocks (max_blocks), fp32 caches and lists whose
+ * per-split share exceeds 8200 ids run the separate selection launch and
+ * the decode launch instead.
  * Requires max_sel >= resa_selection_count(cfg, kv->max_blocks) and
  * ws_bytes >= resa_workspace_bytes(cfg, RESA_OP_SPARSE_STEP, num_requests,
- * kv->max_blocks, max_sel, 0), a workspace whose counters are zero (see
- * resa_workspace_bytes).  Reads q, k_pool, v_pool, desc_pool, block_table,
- * seq_lens (and writes the last block's descriptor when refresh_tail != 0);
- * writes sel_idx, sel_cnt, out [R][H*g][d] float32.
+ * kv->max_blocks, max_sel, 0); the workspace needs no initialisation.
+ * Reads q, k_pool, v_pool, desc_pool, block_table, seq_lens (and writes the
+ * last block's descriptor when refresh_tail != 0); writes sel_idx, sel_cnt,
+ * out [R][H*g][d] float32.
  */
 resa_status resa_sparse_step(const resa_config* cfg, const resa_paged_kv* kv, int32_t num_requests,
                              const void* q, int32_t refresh_tail, int32_t* sel_idx, int32_t* sel_cnt,

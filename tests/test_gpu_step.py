@@ -1,12 +1,13 @@
-"""resa_sparse_step (score, select and sparse attention in one persistent
-launch) against the CPU oracle and against the two-call path
-(resa_score_select + resa_sparse_decode): the same selection id for id, the
-tail descriptor refreshed bit-exactly, and attention outputs within the
+"""resa_sparse_step (scoring, then the selection fused with the split
+attention, then the merge) against the CPU oracle and against the two-call
+path (resa_score_select + resa_sparse_decode): the same selection id for id,
+the tail descriptor refreshed bit-exactly, and attention outputs within the
 output tolerance of the oracle on the selected blocks.  Covers the small
 parity cases (ragged, permuted pools, NaN padding, d = 64, fp32, g = 16,
 mean-pooled scoring, wider local windows, the n_min floor, extra table
-columns), the full-size workloads, repeated calls on one workspace (the
-launch resets its counters) and graph replays."""
+columns), crafted score distributions on both sides of every change of the
+fused kernel's keys per thread and of its fallbacks, the full-size
+workloads, repeated calls on one workspace and graph replays."""
 
 import numpy as np
 import pytest
@@ -17,6 +18,7 @@ import oracle as O
 from synth import WORKLOADS, num_blocks
 from tests import gpu_common as C
 from tests.test_gpu_parity import CASES, make, oracle_scores
+from tests.test_gpu_select import distribution
 
 pytestmark = pytest.mark.gpu
 
@@ -84,8 +86,7 @@ def test_step_refreshes_tail_descriptor(name):
 
 
 def test_step_repeated_calls_on_one_workspace():
-    """Counters and state words return to zero after each launch: several
-    calls with different queries on one workspace, each checked."""
+    """Several calls with different queries on one workspace, each checked."""
     case = make("bf16_extra_table_cols")
     C.run_descriptors(case)
     ms = C.max_sel_for(case)
@@ -159,3 +160,85 @@ def test_step_graph_replays_match_oracle():
             assert torch.equal(st["sel_idx"], si), f"replay {rep}: selection differs"
             assert torch.equal(st["out"], o), f"replay {rep}: output differs"
             check_step_against_oracle(st["case"], st["sel_idx"], st["sel_cnt"], st["out"], tag=f"replay{rep}")
+
+
+def run_crafted(dist, M, seed, budget=(1, 10), splits=0):
+    """Selection of the step on a crafted bf16 score row: with group size 1,
+    a query that is 1 on channel 0 and 0 elsewhere and bf16 descriptors,
+    Eq 4's score of block b is exactly hi_0(b) (every other term is an exact
+    zero), so the row can hold any bf16 distribution.  Checks sel_idx and
+    sel_cnt id for id against the oracle's selection and against
+    resa_score_select, and the attention output against the two calls."""
+    rng = np.random.default_rng(seed)
+    R, H, D = 2, 2, 64
+    Ms = [M, max(1, M - 7)]
+    mb = M
+    P = R * mb
+    cfg = resa.Config(num_kv_heads=H, group_size=1, head_dim=D, dtype=resa.RESA_BF16, budget_num=budget[0],
+                      budget_den=budget[1], num_splits=splits)
+    desc = torch.zeros((P, H, 2, D), dtype=torch.float32)
+    S = {}
+    for r in range(R):
+        for i in range(H):
+            s = torch.from_numpy(distribution(dist, rng, Ms[r])).to(torch.bfloat16).float()
+            s[s == 0] = 1e-3
+            s = s.to(torch.bfloat16).float()
+            S[r, i] = s.numpy().astype(np.float64)
+            rows = torch.arange(Ms[r]) + r * mb
+            desc[rows, i, 0, 0] = s
+            desc[rows, i, 1, 0] = s
+            desc[rows, i, :, 1:] = torch.from_numpy(rng.normal(0, 1, (Ms[r], 2, D - 1)).astype(np.float32))
+    table = (torch.arange(mb, dtype=torch.int32)[None, :] + torch.arange(R, dtype=torch.int32)[:, None] * mb)
+    seq = torch.tensor([m * 16 - 3 for m in Ms], dtype=torch.int32)
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    kv = resa.PagedKV(torch.randn((P, H, 16, D), device="cuda", generator=gen).to(torch.bfloat16),
+                      torch.randn((P, H, D, 16), device="cuda", generator=gen).to(torch.bfloat16),
+                      desc.to(torch.bfloat16).cuda(), table.cuda(), seq.cuda())
+    q = torch.zeros((R, H, D), dtype=torch.float32)
+    q[:, :, 0] = 1.0
+    q = q.to(torch.bfloat16).cuda()
+    ms = resa.selection_count(cfg, M)
+    sel_idx = torch.full((R, H, ms), -7, dtype=torch.int32, device="cuda")
+    sel_cnt = torch.zeros((R, H), dtype=torch.int32, device="cuda")
+    out = torch.full((R, H, D), float("nan"), device="cuda")
+    resa.sparse_step(cfg, kv, q, sel_idx, sel_cnt, out, resa.alloc_workspace(cfg, resa.OP_SPARSE_STEP, R, mb, ms))
+    si2 = torch.full_like(sel_idx, -5)
+    sc2 = torch.zeros_like(sel_cnt)
+    resa.score_select(cfg, kv, q, si2, sc2, resa.alloc_workspace(cfg, resa.OP_SCORE_SELECT, R, mb, ms))
+    out2 = torch.full_like(out, float("nan"))
+    resa.sparse_decode(cfg, kv, q, si2, sc2, out2, resa.alloc_workspace(cfg, resa.OP_SPARSE_DECODE, R, mb, ms))
+    torch.cuda.synchronize()
+    assert torch.equal(sel_idx, si2) and torch.equal(sel_cnt, sc2), f"{dist} M={M}: step and score_select differ"
+    sel_idx, sel_cnt = sel_idx.cpu(), sel_cnt.cpu()
+    for r in range(R):
+        for i in range(H):
+            ref = O.select(S[r, i], cfg.budget_num, cfg.budget_den, cfg.min_blocks, cfg.local_blocks)
+            n = int(sel_cnt[r, i])
+            got = sel_idx[r, i, :n].numpy()
+            assert n == len(ref), f"{dist} r{r} i{i}: count {n} != {len(ref)}"
+            assert np.array_equal(got, ref), \
+                f"{dist} M={Ms[r]} r{r} i{i}: first difference at {np.nonzero(got != ref)[0][:3]}"
+            assert torch.all(sel_idx[r, i, n:] == -1)
+    C.check_out(out.cpu().numpy(), out2.cpu().numpy().astype(np.float64), f"{dist} M={M} vs two calls")
+
+
+# rows on both sides of every change of the fused kernel's keys per thread
+# (2048, 4096 keys) and of its limit (8192 keys; longer rows take the
+# selection launch and the decode launch)
+@pytest.mark.parametrize("M", [20, 300, 2048, 2052, 4096, 4100, 8192, 8196, 16384, 16388])
+@pytest.mark.parametrize("dist", ["normal", "few_levels", "huge_outlier", "clustered_top"])
+def test_step_select_sizes(dist, M):
+    run_crafted(dist, M, seed=M + 3)
+
+
+@pytest.mark.parametrize("dist", ["equal", "two_levels", "mixed_sign_wide", "near_float_max", "tiny"])
+def test_step_select_distributions_16k(dist):
+    run_crafted(dist, 16384, seed=17)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7])
+def test_step_select_long_lists(splits):
+    """A 3/5 budget at 16K blocks: with one split the list (9831 ids) is
+    longer than the fused kernel's LDS list and the two-call path runs; with
+    two or seven splits each split's share fits."""
+    run_crafted("normal", 16384, seed=23 + splits, budget=(3, 5), splits=splits)
