@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(
            num_pool_blocks, scale_log2);
   }
   const size_t prow = ((size_t)r * H + i) * S + s;  // partial row of this workgroup
-  wg_merge_store<T, D, NW, false>(st, mls, G, part_o + prow * G * D, part_ml + prow * G * 2);
+  wg_merge_store<T, D, NW>(st, mls, G, part_o + prow * G * D, part_ml + prow * G * 2);
 }
 
 constexpr int kMergeThreads = 256;

@@ -162,9 +162,8 @@ struct MergeLds {
 
 // Merges the NW wavefronts' states into one partial per query column j < G:
 // part_o[j * D + c] = sum_w 2^(m_w - m) o_w[c], part_ml[2 j] = m = max_w m_w,
-// part_ml[2 j + 1] = sum_w 2^(m_w - m) l_w.  AGENT stores at device scope (for
-// a reader in the same launch).  Contains workgroup barriers.
-template <typename T, int D, int NW, bool AGENT>
+// part_ml[2 j + 1] = sum_w 2^(m_w - m) l_w.  Contains workgroup barriers.
+template <typename T, int D, int NW>
 __device__ __forceinline__ void wg_merge_store(WaveAttn<T, D>& st, MergeLds<NW, D>& ml, int G,
                                                float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int NT = WaveAttn<T, D>::NT;
@@ -205,18 +204,10 @@ __device__ __forceinline__ void wg_merge_store(WaveAttn<T, D>& st, MergeLds<NW, 
           l += wt * ml.l[w][j];
         }
       }
-      if constexpr (AGENT) {
-        store_agent(reinterpret_cast<uint32_t*>(part_o) + j * D + c, __float_as_uint(o));
-        if (c == 0) {
-          store_agent(reinterpret_cast<uint32_t*>(part_ml) + j * 2, __float_as_uint(mw));
-          store_agent(reinterpret_cast<uint32_t*>(part_ml) + j * 2 + 1, __float_as_uint(l));
-        }
-      } else {
-        part_o[j * D + c] = o;
-        if (c == 0) {
-          part_ml[j * 2] = mw;
-          part_ml[j * 2 + 1] = l;
-        }
+      part_o[j * D + c] = o;
+      if (c == 0) {
+        part_ml[j * 2] = mw;
+        part_ml[j * 2 + 1] = l;
       }
     }
     __syncthreads();
@@ -264,23 +255,6 @@ struct PlainPartials {
   const float* __restrict__ ml;
   __device__ float2 load_ml(size_t row) const { return *reinterpret_cast<const float2*>(ml + row * 2); }
   __device__ floatx4_t load_o(size_t off) const { return *reinterpret_cast<const floatx4_t*>(o + off); }
-};
-
-// Partials written by other workgroups of the same launch: device-scope
-// buffer loads (cache policy sc1) from bases uniform over the workgroup.
-struct AgentPartials {
-  __amdgpu_buffer_rsrc_t o, ml;
-  __device__ AgentPartials(const float* po, const float* pml, uint32_t o_bytes, uint32_t ml_bytes)
-      : o(__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(po), (short)0, (int)o_bytes, 0x00020000)),
-        ml(__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(pml), (short)0, (int)ml_bytes, 0x00020000)) {}
-  __device__ float2 load_ml(size_t row) const {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(ml, (uint32_t)(row * 8), 0, 16);
-    return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
-  }
-  __device__ floatx4_t load_o(size_t off) const {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(o, (uint32_t)(off * 4), 0, 16);
-    return floatx4_t{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
-  }
 };
 
 // One output float4 (lane group of kMergeParts): S partials of partial row

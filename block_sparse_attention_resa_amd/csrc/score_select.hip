@@ -23,6 +23,7 @@
 // a CU, and the fused form measured slower on every workload.
 #include "desc_unit.h"
 #include "score_core.h"
+#include "select_core.h"
 
 namespace resa {
 namespace {
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const uint32_t* __restrict__
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
   KeyRuns<NT, KPT> kr;
-  kr.template prefetch<false>(keys + ((size_t)r * H + i) * key_stride, key_stride);  // in flight with seq_lens
+  kr.prefetch(keys + ((size_t)r * H + i) * key_stride, key_stride);  // in flight with seq_lens
   const int L = clampi(seq_lens[r], 0, max_blocks * kBlock);
   const int M = (L + kBlock - 1) / kBlock;
   int32_t* out = sel_idx + ((size_t)r * H + i) * max_sel;

@@ -1,7 +1,5 @@
 // Top-n block selection over order-preserving 32-bit score keys, run by one
-// workgroup per (request, KV head), and the device-scope
-// exchange helpers of the kernels that hand keys from workgroup to
-// workgroup inside one launch.
+// workgroup per (request, KV head).
 //
 // "Rectified Sparse Attention" analysis page (paper-graph-ui), §3.4.1 Eq 5
 // (the n - n_local highest-scoring older blocks; ties here go to the lower
@@ -24,38 +22,6 @@
 #include "resa_internal.h"
 
 namespace resa {
-
-// ------------------------------------------------- device-scope exchange
-//
-// Data handed between workgroups of one launch is written with device-scope
-// stores (cache policy sc1: written through to the device coherence point),
-// the writer waits for their completion before it signals with an atomic,
-// and the reader, after seeing the signal, reads with device-scope loads, so
-// no write-back or invalidation of whole caches is needed.
-
-__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
-// Word quadruple `quad` of a row of `nwords` 32-bit words, read with a
-// 16-byte buffer load at device scope (cache policy sc1).  The row base is
-// uniform over the workgroup; reads past the row return zero.
-__device__ __forceinline__ uint4 load16_agent(const uint32_t* row, int nwords, int quad) {
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(row), (short)0, nwords * 4, 0x00020000);
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, quad * 16, 0, 16);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-// Wait until every vector memory access this lane issued has completed
-// (stores and atomics included): vmcnt(0), other counters unconstrained.
-__device__ __forceinline__ void wait_vm_all() {
-  __builtin_amdgcn_s_waitcnt(0x0f70);
-  asm volatile("" ::: "memory");
-}
-
 
 constexpr int kDigitBits = 12;  // histogram pass: 4096 bins
 constexpr int kBins = 1 << kDigitBits;
@@ -168,12 +134,8 @@ struct KeyRuns {
   uint32_t in_mask;  // KPT > 0: bit j set when this thread's key j is a candidate
   bool full;         // KPT > 0, uniform over the wavefront: every key of every lane is a candidate
   bool any;          // KPT > 0, uniform over the wavefront: some lane holds a candidate
-  // SAME_LAUNCH: the keys were written by other workgroups of the same
-  // launch, so they are read at device scope (16-byte buffer loads with the
-  // device-scope cache policy), never from a line an earlier read left in a
-  // nearer cache.  Keys written by an earlier launch are read with plain
-  // 16-byte loads: the launch boundary has made them visible.
-  template <bool SAME_LAUNCH>
+  // The keys were written by an earlier launch (the launch boundary has made
+  // them visible), so they are read with plain 16-byte loads.
   __device__ void prefetch(const uint32_t* kr, int row_stride) {
     row = kr;
     if constexpr (KPT > 0) {
@@ -182,7 +144,7 @@ struct KeyRuns {
       for (int v = 0; v < KPT / 4; ++v) {
         const int idx = (int)threadIdx.x * (KPT / 4) + v;
         const int q = idx < last ? idx : last;
-        const uint4 x = SAME_LAUNCH ? load16_agent(kr, row_stride, q) : *reinterpret_cast<const uint4*>(kr + 4 * q);
+        const uint4 x = *reinterpret_cast<const uint4*>(kr + 4 * q);
         reg[4 * v] = x.x;
         reg[4 * v + 1] = x.y;
         reg[4 * v + 2] = x.z;
@@ -223,7 +185,7 @@ struct KeyRuns {
   }
   __device__ uint32_t key(int j) const {
     if constexpr (KPT > 0) return reg[j];
-    else return load_agent(row + threadIdx.x + j * NT);
+    else return row[threadIdx.x + j * NT];
   }
   __device__ int nrounds() const { return KPT > 0 ? KPT : rounds; }
 };

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64 * NW) void select_decode_kernel(
 
   // the row's keys and the group's queries are in flight together
   KeyRuns<NT, KPT> kr;
-  kr.template prefetch<false>(keys + row * key_stride, key_stride);
+  kr.prefetch(keys + row * key_stride, key_stride);
   typename F::Q qf;
   F::load_q(qf, q + row * G * D, col, quad, G);
 
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(64 * NW) void select_decode_kernel(
   st.run([&](int p) { return list[p - beg]; }, wb, we_cap, we, qf, k_pool, v_pool, table + (size_t)r * max_blocks,
          H, i, L, max_blocks, num_pool_blocks, scale_log2);
   const size_t prow = row * S + s;
-  wg_merge_store<T, D, NW, false>(st, lds.mls, G, part_o + prow * G * D, part_ml + prow * G * 2);
+  wg_merge_store<T, D, NW>(st, lds.mls, G, part_o + prow * G * D, part_ml + prow * G * 2);
 }
 
 // Keys per thread of the fused kernel for rows of `key_stride` keys, or 0
