@@ -392,7 +392,7 @@ def main(argv=None):
     gbps = ab["total"] / (us_layer * 1e-6) / 1e9
     dec_bytes = ab["kv"] + ab["q"] + ab["out"]
     dec_gbps = dec_bytes / (t_dec * 1e-6) / 1e9
-    khash = source_hash("decode.hip", "attn_frag.h", "resa_internal.h")
+    khash = source_hash("decode.hip", "decode_core.h", "attn_frag.h", "resa_internal.h")
     traffic, trace = measured_traffic(khash)
     trace_us = trace.get("decode") if isinstance(trace, dict) else None
 
