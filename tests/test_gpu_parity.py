@@ -35,6 +35,18 @@ CASES = {
 }
 
 
+def run_step(case):
+    """resa_sparse_step on a case (no tail refresh): (sel_idx, sel_cnt, out)."""
+    R, H, HG, d = case.R, case.spec.num_kv_heads, case.spec.num_q_heads, case.spec.head_dim
+    ms = C.max_sel_for(case)
+    sel_idx = torch.full((R, H, ms), -7, dtype=torch.int32, device="cuda")
+    sel_cnt = torch.full((R, H), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((R, HG, d), float("nan"), device="cuda")
+    ws = resa.alloc_workspace(case.cfg, resa.OP_SPARSE_STEP, R, case.kv.max_blocks, ms)
+    resa.sparse_step(case.cfg, case.kv, case.inp.q, sel_idx, sel_cnt, out, ws)
+    return sel_idx, sel_cnt, out
+
+
 def make(name, seed=11):
     kw = dict(CASES[name])
     spec = kw.pop("spec")
@@ -256,10 +268,14 @@ def test_zero_length_request():
     sel_idx, sel_cnt, _ = C.run_score_select(case)
     sp = C.run_sparse(case, sel_idx, sel_cnt)
     de = C.run_dense(case)
+    st_idx, st_cnt, st_out = run_step(case)
     torch.cuda.synchronize()
     assert int(sel_cnt[0].abs().sum()) == 0
     assert bool((sel_idx[0] == -1).all())
     assert float(sp[0].abs().max()) == 0.0 and float(de[0].abs().max()) == 0.0
+    # the step call: the same selection, a zero output for the empty request
+    assert torch.equal(st_idx, sel_idx) and torch.equal(st_cnt, sel_cnt)
+    assert torch.equal(st_out, sp)
     g = spec.group_size
     for i in range(spec.num_kv_heads):
         ref = O.dense(C.group_q(case, 1, i), C.keys_of(case, 1, i), C.values_of(case, 1, i), 700,
@@ -368,8 +384,9 @@ def test_out_of_range_device_values_are_clamped():
         sel, cnt, sc = C.run_score_select(c)
         sp = C.run_sparse(c, sel, cnt)
         de = C.run_dense(c)
+        st_sel, st_cnt, st_out = run_step(c)
         torch.cuda.synchronize()
-        return [sel, cnt, sc, sp, de]
+        return [sel, cnt, sc, sp, de, st_sel, st_cnt, st_out]
 
     def same(a, b, tag):
         for x, y in zip(a, b):
