@@ -222,3 +222,34 @@ def test_noalloc_refuses_more_than_its_scratch_before_any_gpu_call(lib):
     assert st == 3
     assert lib.resa_sparse_decode_noalloc(ctypes.byref(c), ctypes.byref(kv), 1, FAKE, FAKE, FAKE, 0, FAKE, None) == 1
     assert lib.resa_sparse_decode_noalloc(None, ctypes.byref(kv), 1, FAKE, FAKE, FAKE, 16, FAKE, None) == 1
+
+
+def test_step_workspace_and_argument_checks(lib):
+    """resa_sparse_step's workspace holds the score keys and the sparse
+    decode's partials (it needs no initialisation), and its host checks
+    refuse bad arguments before anything is launched (fake pointers)."""
+    c = cfg()
+    for R, mb, ms in [(1, 32, 16), (1, 16384, 1639), (8, 4096, 410), (3, 100, 20)]:
+        step = lib.resa_workspace_bytes(ctypes.byref(c), B.OP_SPARSE_STEP, R, mb, ms, 0)
+        parts = (lib.resa_workspace_bytes(ctypes.byref(c), B.OP_SCORE_SELECT, R, mb, ms, 0) +
+                 lib.resa_workspace_bytes(ctypes.byref(c), B.OP_SPARSE_DECODE, R, mb, ms, 0))
+        assert step == parts and step > 0
+    assert lib.resa_workspace_bytes(ctypes.byref(c), B.OP_SPARSE_STEP, 1, 32, 0, 0) == 0
+    kv = kv_ok()
+    n_full = lib.resa_selection_count(ctypes.byref(c), 32)
+    ws = lib.resa_workspace_bytes(ctypes.byref(c), B.OP_SPARSE_STEP, 1, 32, n_full, 0)
+    call = lambda q, si, sc, ms, out, wsp, wsb: lib.resa_sparse_step(  # noqa: E731
+        ctypes.byref(c), ctypes.byref(kv), 1, q, 1, si, sc, ms, out, wsp, wsb, None)
+    assert call(None, FAKE, FAKE, n_full, FAKE, FAKE, ws) == 1
+    assert call(FAKE_ODD, FAKE, FAKE, n_full, FAKE, FAKE, ws) == 1
+    assert call(FAKE, None, FAKE, n_full, FAKE, FAKE, ws) == 1
+    assert call(FAKE, FAKE, None, n_full, FAKE, FAKE, ws) == 1
+    assert call(FAKE, FAKE, FAKE, n_full - 1, FAKE, FAKE, ws) == 1  # sel_idx rows too short
+    assert call(FAKE, FAKE, FAKE, n_full, None, FAKE, ws) == 1
+    assert call(FAKE, FAKE, FAKE, n_full, FAKE_ODD, FAKE, ws) == 1
+    assert call(FAKE, FAKE, FAKE, n_full, FAKE, None, ws) == 3
+    assert call(FAKE, FAKE, FAKE, n_full, FAKE, FAKE, ws - 1) == 3
+    assert lib.resa_sparse_step(ctypes.byref(c), ctypes.byref(kv), 0, FAKE, 1, FAKE, FAKE, n_full, FAKE, None, 0,
+                                None) == 0  # no requests: nothing to do
+    kv.v_pool = None  # the attention reads v_pool
+    assert call(FAKE, FAKE, FAKE, n_full, FAKE, FAKE, ws) == 1
