@@ -242,3 +242,35 @@ def test_step_select_long_lists(splits):
     longer than the fused kernel's LDS list and the two-call path runs; with
     two or seven splits each split's share fits."""
     run_crafted("normal", 16384, seed=23 + splits, budget=(3, 5), splits=splits)
+
+
+@pytest.mark.parametrize("splits", [1, 5, 64])
+def test_step_explicit_splits_and_wide_list_rows(splits):
+    """An explicit split count and sel_idx rows wider than the selection
+    (positions past n must read -1): the step against the two calls, id for
+    id and bit for bit (both split the list the same way), and against the
+    oracle."""
+    case = make("bf16_ragged_r3_perm_nan")
+    case.cfg.num_splits = splits
+    C.run_descriptors(case)
+    R, H, HG, d = case.R, case.spec.num_kv_heads, case.spec.num_q_heads, case.spec.head_dim
+    ms = C.max_sel_for(case) + 37
+    si = torch.full((R, H, ms), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((R, H), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((R, HG, d), float("nan"), device="cuda")
+    resa.sparse_step(case.cfg, case.kv, case.inp.q, si, sc, out,
+                     resa.alloc_workspace(case.cfg, resa.OP_SPARSE_STEP, R, case.kv.max_blocks, ms))
+    si2 = torch.full_like(si, -5)
+    sc2 = torch.full_like(sc, -5)
+    resa.score_select(case.cfg, case.kv, case.inp.q, si2, sc2,
+                      resa.alloc_workspace(case.cfg, resa.OP_SCORE_SELECT, R, case.kv.max_blocks, ms))
+    out2 = torch.full_like(out, float("nan"))
+    resa.sparse_decode(case.cfg, case.kv, case.inp.q, si2, sc2, out2,
+                       resa.alloc_workspace(case.cfg, resa.OP_SPARSE_DECODE, R, case.kv.max_blocks, ms))
+    torch.cuda.synchronize()
+    assert torch.equal(si, si2) and torch.equal(sc, sc2)
+    assert torch.equal(out, out2)
+    for r in range(R):
+        for i in range(H):
+            assert bool((si[r, i, int(sc[r, i]):] == -1).all())
+    check_step_against_oracle(case, si, sc, out, tag=f"splits{splits}")
