@@ -237,11 +237,12 @@ def test_step_select_distributions_16k(dist):
 
 
 @pytest.mark.parametrize("splits", [1, 2, 7])
-def test_step_select_long_lists(splits):
-    """A 3/5 budget at 16K blocks: with one split the list (9831 ids) is
-    longer than the fused kernel's LDS list and the two-call path runs; with
-    two or seven splits each split's share fits."""
-    run_crafted("normal", 16384, seed=23 + splits, budget=(3, 5), splits=splits)
+@pytest.mark.parametrize("M", [8192, 16384])
+def test_step_select_long_lists(M, splits):
+    """A 3/5 budget at 8192 blocks: the list (4916 ids) fits the fused
+    kernel's LDS list even with one split; at 16384 blocks (9831 ids) every
+    split count takes the two-call kernels."""
+    run_crafted("normal", M, seed=23 + splits, budget=(3, 5), splits=splits)
 
 
 @pytest.mark.parametrize("splits", [1, 5, 64])
