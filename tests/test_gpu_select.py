@@ -117,3 +117,11 @@ def test_select_distributions_16k(dist):
 @pytest.mark.parametrize("dist", ["normal", "few_levels", "huge_outlier"])
 def test_select_sizes(dist, M):
     run_case(dist, M, seed=M)
+
+
+# short rows, every distribution: fewer candidates than one histogram pass
+# needs, and rows of 1024 to 2048 keys (the 512-thread selection)
+@pytest.mark.parametrize("M", [60, 66, 1024, 1025, 2048])
+@pytest.mark.parametrize("dist", DISTS)
+def test_select_short_rows(dist, M):
+    run_case(dist, M, seed=7 * M + 1)
