@@ -28,12 +28,14 @@
 namespace resa {
 namespace {
 
-constexpr int kScoreUnroll = 4;     // blocks per thread (passes) in the scoring kernel
+constexpr int kScoreFill = 256;     // scoring workgroups that keep the 256 CUs busy
 constexpr int kScoreThreads = 256;  // threads of a scoring workgroup, at most
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectSmall = 512;  // threads of the selection of rows of up to 4096 keys
 
-template <typename T, int D, int MODE, int MAXG>
+// U: blocks per thread (passes), 4, or 2 or 1 for grids too small to give
+// every CU a workgroup at 4.
+template <typename T, int D, int MODE, int MAXG, int U>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const T* __restrict__ q, const T* desc, const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
     uint32_t* __restrict__ keys, float* __restrict__ scores, int H, int HW, int G, int max_blocks,
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   const bool head_ok = head < H;
   const int bsub = grp / HW;
   const int bpi = blockDim.x / (CH * HW);  // blocks per pass
-  const int wg_blocks = bpi * kScoreUnroll;
+  const int wg_blocks = bpi * U;
   const int wg_b0 = blockIdx.x * wg_blocks;
   uint32_t* key_row = keys + ((size_t)r * H + (head_ok ? head : 0)) * key_stride;
   float* score_row = scores ? scores + ((size_t)r * H + (head_ok ? head : 0)) * max_blocks : nullptr;
@@ -105,10 +107,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   }
   const int L = clampi(seq_len, 0, max_blocks * kBlock);
   const int M = (L + kBlock - 1) / kBlock;
-  uint4 buf[kScoreUnroll][2];
-  int bl[kScoreUnroll];
+  uint4 buf[U][2];
+  int bl[U];
 #pragma unroll
-  for (int u = 0; u < kScoreUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int bo = u * bpi + bsub;
     const int b = wg_b0 + bo;
     bl[u] = b;
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
   }
 
 #pragma unroll
-  for (int u = 0; u < kScoreUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     float vals[VPL];
     CL::unpack(buf[u][0], buf[u][1], vals);
     float acc = 0.f;
@@ -261,18 +263,29 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
   }
   const int unit = CH * HW;  // threads per block of all the group's heads
   int m = min_blocks_per_pass(unit);
-  while (unit * m * 2 <= kScoreThreads && m * 2 * kScoreUnroll <= 64) m *= 2;
+  while (unit * m * 2 <= kScoreThreads && m * 2 * 4 <= 64) m *= 2;
   const int threads = unit * m;  // <= kScoreThreads
   const int bpi = m;
-  const int blocks_per_wg = bpi * kScoreUnroll;  // <= 64: one table entry per lane
+  // Four passes per thread, unless the grid would then leave CUs idle (short
+  // rows, few requests): fewer passes and more workgroups there.
+  const long long groups = (long long)a.R * ((a.H + HW - 1) / HW);
+  int U = 4;
+  while (U > 1 && groups * ((a.max_blocks + bpi * U - 1) / (bpi * U)) < kScoreFill) U /= 2;
+  const int blocks_per_wg = bpi * U;  // <= 64: one table entry per lane
   const int wgs = (a.max_blocks + blocks_per_wg - 1) / blocks_per_wg;
   const size_t lds = (size_t)HW * 2 * D * sizeof(float);
   dim3 grid((unsigned)(wgs + (a.refresh_tail ? 1 : 0)), (unsigned)a.R, (unsigned)((a.H + HW - 1) / HW));
-#define RESA_SCORE_LAUNCH(MODE, MAXG)                                                                        \
-  hipLaunchKernelGGL((score_kernel<T, D, MODE, MAXG>), grid, dim3(threads), lds, stream,                     \
+#define RESA_SCORE_LAUNCH_U(MODE, MAXG, UU)                                                                  \
+  hipLaunchKernelGGL((score_kernel<T, D, MODE, MAXG, UU>), grid, dim3(threads), lds, stream,                 \
                      static_cast<const T*>(a.q), static_cast<const T*>(a.desc_pool), a.table, a.seq_lens, a.keys, \
                      a.scores, a.H, HW, a.G, a.max_blocks, a.num_pool_blocks, static_cast<const T*>(a.k_pool), \
                      static_cast<T*>(const_cast<void*>(a.desc_pool)), wgs, a.key_stride)
+#define RESA_SCORE_LAUNCH(MODE, MAXG)                      \
+  do {                                                     \
+    if (U == 4) RESA_SCORE_LAUNCH_U(MODE, MAXG, 4);        \
+    else if (U == 2) RESA_SCORE_LAUNCH_U(MODE, MAXG, 2);   \
+    else RESA_SCORE_LAUNCH_U(MODE, MAXG, 1);               \
+  } while (0)
   if (a.G <= 8) {
     if (a.mode == 0) RESA_SCORE_LAUNCH(0, 8);
     else RESA_SCORE_LAUNCH(1, 8);
@@ -281,6 +294,7 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
     else RESA_SCORE_LAUNCH(1, 16);
   }
 #undef RESA_SCORE_LAUNCH
+#undef RESA_SCORE_LAUNCH_U
   return hipGetLastError();
 }
 
