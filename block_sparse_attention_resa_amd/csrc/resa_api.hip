@@ -74,7 +74,9 @@ int splits_for(const resa_config* c, int op, int R, int max_blocks, int max_sel,
   if (op == RESA_OP_SPARSE_DECODE) {
     len = max_sel;
     target = 256;  // 8-wavefront workgroups: about one per CU
-    min_share = kDecodeWaves;
+    // at least four list positions per split: on short lists more splits
+    // (half a block per wavefront) still shorten the call (16K: 9.3 -> 8.7 us)
+    min_share = kDecodeWaves / 2;
   } else if (op == RESA_OP_DENSE_DECODE) {
     len = max_blocks;
     target = 256;
