@@ -96,8 +96,19 @@ def test_graph_replay_matches_eager():
     several layers) captured in a HIP graph: every replay, with eager work and
     synchronisations in between, reproduces the eager results bit for bit,
     and every replay's selections and outputs match the oracle."""
-    spec = WORKLOADS["qwen7b_ctx32k_b1"]
-    cases = [C.make_case(spec, seed=300 + l) for l in range(3)]
+    graph_replay_case(WORKLOADS["qwen7b_ctx32k_b1"], seeds=(300, 301, 302), reps=4)
+
+
+@pytest.mark.timeout(900)
+def test_graph_replay_matches_eager_256k():
+    """The benchmark's own configuration: two layers of the 256K workload
+    (16384 blocks per head, the 1024-thread selection and 64 decode splits
+    per head), the two calls captured in one HIP graph and replayed twice."""
+    graph_replay_case(WORKLOADS["qwen7b_ctx256k_l28"], seeds=(2024, 2025), reps=2)
+
+
+def graph_replay_case(spec, seeds, reps):
+    cases = [C.make_case(spec, seed=sd) for sd in seeds]
     R, H, g, d = 1, spec.num_kv_heads, spec.group_size, spec.head_dim
     state = []
     for case in cases:
@@ -129,7 +140,7 @@ def test_graph_replay_matches_eager():
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
-    for rep in range(4):
+    for rep in range(reps):
         for st in state:  # eager work between replays
             st["out"].fill_(float("nan"))
             st["sel_idx"].fill_(-9)
