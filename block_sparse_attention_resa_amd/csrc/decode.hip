@@ -12,7 +12,8 @@
 // consecutive sub-ranges and each keeps its own online-softmax state
 // (decode_core.h), merged through LDS into one partial (m, l, o) per query
 // head.  A second kernel merges the splits' partials with their log-sum-exp
-// weights.
+// weights; with one split per row (large batches) the workgroup normalises
+// and writes the output itself and no merge is launched.
 #include "decode_core.h"
 #include "resa_internal.h"
 
@@ -24,7 +25,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k_pool, const T* __restrict__ v_pool,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, int max_sel, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int H, int G, int max_blocks, int num_pool_blocks, int S, float scale_log2) {
+    float* __restrict__ out, int H, int G, int max_blocks, int num_pool_blocks, int S, float scale_log2) {
   using F = Frag<T, D>;
   __shared__ MergeLds<NW, D> mls;
 
@@ -69,7 +70,9 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(
            num_pool_blocks, scale_log2);
   }
   const size_t prow = ((size_t)r * H + i) * S + s;  // partial row of this workgroup
-  wg_merge_store<T, D, NW>(st, mls, G, part_o + prow * G * D, part_ml + prow * G * 2);
+  // a row's only split writes the output itself (no merge launch follows)
+  wg_merge_store<T, D, NW>(st, mls, G, part_o + prow * G * D, part_ml + prow * G * 2,
+                           S == 1 ? out + ((size_t)r * H + i) * G * D : nullptr);
 }
 
 constexpr int kMergeThreads = 256;
@@ -115,16 +118,16 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   if (a.sel_idx) {
     hipLaunchKernelGGL((decode_kernel<T, D, true, NW>), grid, block, 0, stream, static_cast<const T*>(a.q),
                        static_cast<const T*>(a.k_pool), static_cast<const T*>(a.v_pool), a.table, a.seq_lens,
-                       a.sel_idx, a.sel_cnt, a.max_sel, a.part_o, a.part_ml, a.H, a.G, a.max_blocks,
+                       a.sel_idx, a.sel_cnt, a.max_sel, a.part_o, a.part_ml, a.out, a.H, a.G, a.max_blocks,
                        a.num_pool_blocks, a.splits, a.scale_log2);
   } else {
     hipLaunchKernelGGL((decode_kernel<T, D, false, NW>), grid, block, 0, stream, static_cast<const T*>(a.q),
                        static_cast<const T*>(a.k_pool), static_cast<const T*>(a.v_pool), a.table, a.seq_lens,
-                       nullptr, nullptr, 0, a.part_o, a.part_ml, a.H, a.G, a.max_blocks, a.num_pool_blocks,
+                       nullptr, nullptr, 0, a.part_o, a.part_ml, a.out, a.H, a.G, a.max_blocks, a.num_pool_blocks,
                        a.splits, a.scale_log2);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.splits == 1) return e;  // one split: the decode wrote the output
   return launch_merge(a.part_o, a.part_ml, a.out, a.R, a.H, a.G, a.D, a.splits, a.G, 1, stream);
 }
 

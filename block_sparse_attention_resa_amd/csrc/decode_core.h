@@ -162,10 +162,14 @@ struct MergeLds {
 
 // Merges the NW wavefronts' states into one partial per query column j < G:
 // part_o[j * D + c] = sum_w 2^(m_w - m) o_w[c], part_ml[2 j] = m = max_w m_w,
-// part_ml[2 j + 1] = sum_w 2^(m_w - m) l_w.  Contains workgroup barriers.
+// part_ml[2 j + 1] = sum_w 2^(m_w - m) l_w.  With `out` not null (the row's
+// only split) it writes the normalised output out[j * D + c] = part_o / l
+// instead, the same operations as the merge of a single partial.  Contains
+// workgroup barriers.
 template <typename T, int D, int NW>
 __device__ __forceinline__ void wg_merge_store(WaveAttn<T, D>& st, MergeLds<NW, D>& ml, int G,
-                                               float* __restrict__ part_o, float* __restrict__ part_ml) {
+                                               float* __restrict__ part_o, float* __restrict__ part_ml,
+                                               float* __restrict__ out = nullptr) {
   constexpr int NT = WaveAttn<T, D>::NT;
   constexpr int CG = MergeLds<NW, D>::kCols;
   constexpr int NTH = 64 * NW;
@@ -204,10 +208,15 @@ __device__ __forceinline__ void wg_merge_store(WaveAttn<T, D>& st, MergeLds<NW, 
           l += wt * ml.l[w][j];
         }
       }
-      part_o[j * D + c] = o;
-      if (c == 0) {
-        part_ml[j * 2] = mw;
-        part_ml[j * 2 + 1] = l;
+      if (out) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        out[j * D + c] = o * inv;
+      } else {
+        part_o[j * D + c] = o;
+        if (c == 0) {
+          part_ml[j * 2] = mw;
+          part_ml[j * 2 + 1] = l;
+        }
       }
     }
     __syncthreads();

@@ -51,7 +51,8 @@ __global__ __launch_bounds__(64 * NW) void select_decode_kernel(
     const uint32_t* __restrict__ keys, int key_stride, const T* __restrict__ q, const T* __restrict__ k_pool,
     const T* __restrict__ v_pool, const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
     int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt, int max_sel, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int H, int G, int max_blocks, int num_pool_blocks, int S, float scale_log2,
+    float* __restrict__ part_ml, float* __restrict__ out, int H, int G, int max_blocks, int num_pool_blocks, int S,
+    float scale_log2,
     int budget_num, int budget_den, int min_blocks, int local_blocks) {
   constexpr int NT = 64 * NW;
   using F = Frag<T, D>;
@@ -139,7 +140,8 @@ __global__ __launch_bounds__(64 * NW) void select_decode_kernel(
   st.run([&](int p) { return list[p - beg]; }, wb, we_cap, we, qf, k_pool, v_pool, table + (size_t)r * max_blocks,
          H, i, L, max_blocks, num_pool_blocks, scale_log2);
   const size_t prow = row * S + s;
-  wg_merge_store<T, D, NW>(st, lds.mls, G, part_o + prow * G * D, part_ml + prow * G * 2);
+  wg_merge_store<T, D, NW>(st, lds.mls, G, part_o + prow * G * D, part_ml + prow * G * 2,
+                           S == 1 ? out + row * G * D : nullptr);  // one split: the output itself
 }
 
 // Keys per thread of the fused kernel for rows of `key_stride` keys, or 0
@@ -158,7 +160,7 @@ hipError_t launch_select_decode_t(const ScoreArgs& sa, const DecodeArgs& da, int
   hipLaunchKernelGGL((select_decode_kernel<T, D, kStepNW, KPT>), grid, dim3(kStepNT), 0, stream, sa.keys,        \
                      sa.key_stride, static_cast<const T*>(da.q), static_cast<const T*>(da.k_pool),                \
                      static_cast<const T*>(da.v_pool), da.table, da.seq_lens, sa.sel_idx, sa.sel_cnt, sa.max_sel, \
-                     da.part_o, da.part_ml, da.H, da.G, da.max_blocks, da.num_pool_blocks, da.splits,              \
+                     da.part_o, da.part_ml, da.out, da.H, da.G, da.max_blocks, da.num_pool_blocks, da.splits,     \
                      da.scale_log2, sa.budget_num, sa.budget_den, sa.min_blocks, sa.local_blocks)
   switch (kpt) {
     case 4: RESA_SELDEC_LAUNCH(4); break;
@@ -187,7 +189,7 @@ hipError_t launch_step(const ScoreArgs& sa, const DecodeArgs& da, hipStream_t st
   const int kpt = step_kpt(sa.key_stride);
   e = da.D == 128 ? launch_select_decode_t<bf16_t, 128>(sa, da, kpt, stream)
                   : launch_select_decode_t<bf16_t, 64>(sa, da, kpt, stream);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || da.splits == 1) return e;  // one split: the attention wrote the output
   return launch_merge(da.part_o, da.part_ml, da.out, da.R, da.H, da.G, da.D, da.splits, da.G, 1, stream);
 }
 

@@ -417,3 +417,40 @@ def test_out_of_range_device_values_are_clamped():
     b = C.run_sparse(case, sel_c, cnt_c)
     torch.cuda.synchronize()
     assert torch.equal(a, b), "selected ids and counts"
+
+
+def test_large_batch_single_split():
+    """64 requests x 4 KV heads: the automatic split count is one, so the
+    sparse decode, the dense decode and the step write their outputs from
+    the attention workgroups (no merge launch).  All three against the
+    oracle, and the sparse decode against a run forced to two splits (merge
+    launch) within rounding."""
+    import dataclasses
+
+    R = 64
+    spec = BF.with_(num_requests=R, seq_lens=tuple(300 + 37 * r for r in range(R)))
+    case = C.make_case(spec, 17)
+    ms = C.max_sel_for(case)
+    assert resa.num_splits(case.cfg, resa.OP_SPARSE_DECODE, R, case.kv.max_blocks, ms) == 1
+    assert resa.num_splits(case.cfg, resa.OP_DENSE_DECODE, R, case.kv.max_blocks) == 1
+    C.run_descriptors(case)
+    sel_idx, sel_cnt, _ = C.run_score_select(case)
+    sp = C.run_sparse(case, sel_idx, sel_cnt)
+    de = C.run_dense(case)
+    st_idx, st_cnt, st_out = run_step(case)
+    two = dataclasses.replace(case, cfg=dataclasses.replace(case.cfg, num_splits=2))
+    sp2 = C.run_sparse(two, sel_idx, sel_cnt)
+    torch.cuda.synchronize()
+    assert torch.equal(st_idx, sel_idx) and torch.equal(st_cnt, sel_cnt)
+    assert torch.equal(st_out, sp), "step and two calls split the list the same way"
+    C.check_out(sp.cpu().numpy(), sp2.cpu().numpy().astype(np.float64), "one split against two")
+    lists = C.sel_lists(sel_idx, sel_cnt)
+    g = spec.group_size
+    scale = C.sm_scale(case.cfg)
+    for r in range(0, R, 9):
+        L = case.inp.seq_lens[r]
+        for i in range(spec.num_kv_heads):
+            q, K, V = C.group_q(case, r, i), C.keys_of(case, r, i), C.values_of(case, r, i)
+            C.check_out(sp[r, i * g:(i + 1) * g].cpu().numpy(), O.attend(q, K, V, L, lists[r][i], scale),
+                        f"sparse r{r} i{i}")
+            C.check_out(de[r, i * g:(i + 1) * g].cpu().numpy(), O.dense(q, K, V, L, scale), f"dense r{r} i{i}")
