@@ -79,11 +79,10 @@ constexpr int kMergeThreads = 256;
 constexpr long long kMergeMaxGrid = 1 << 20;  // workgroups of one merge launch
 
 // Log-sum-exp merge of split partials (decode_core.h), one output float4 per
-// sixteen lanes.  64-bit thread index; the grid strides over the rows when
-// it is capped (rows * C4 * kMergeParts may exceed 2^31).  The stride is a
-// multiple of kMergeParts, so the sixteen lanes of a DPP row always share
-// one row and leave the loop together.
-template <int D>
+// P lanes.  64-bit thread index; the grid strides over the rows when it is
+// capped (rows * C4 * P may exceed 2^31).  The stride is a multiple of P, so
+// the P lanes of a group always share one row and leave the loop together.
+template <int D, int P>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part_o,
                                                               const float* __restrict__ part_ml,
                                                               float* __restrict__ out, int H, int G, int S,
@@ -92,14 +91,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   constexpr int C4 = D / 4;  // float4 per output row
   const PlainPartials pp{part_o, part_ml};
   const long long stride = (long long)gridDim.x * kMergeThreads;
-  for (long long g = (long long)blockIdx.x * kMergeThreads + threadIdx.x; g < total_rows * C4 * kMergeParts;
-       g += stride) {
-    const int part = (int)(g % kMergeParts);
-    const int c4 = (int)((g / kMergeParts) % C4);
-    const long long grow = g / (kMergeParts * C4);  // (r, i, row) flattened
+  for (long long g = (long long)blockIdx.x * kMergeThreads + threadIdx.x; g < total_rows * C4 * P; g += stride) {
+    const int part = (int)(g % P);
+    const int c4 = (int)((g / P) % C4);
+    const long long grow = g / (P * C4);  // (r, i, row) flattened
     const int row = (int)(grow % rows_per_head);
     const long long ri = grow / rows_per_head;  // r * H + i
-    const floatx4_t v = merge_float4<D>(pp, (size_t)ri * S, S, rows_per_head, row, c4, part);
+    const floatx4_t v = merge_float4<D, P>(pp, (size_t)ri * S, S, rows_per_head, row, c4, part);
     if (part == 0) {
       const long long r = ri / H;
       const int i = (int)(ri % H);
@@ -109,6 +107,33 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
       *reinterpret_cast<floatx4_t*>(dst) = v;
     }
   }
+}
+
+template <int D, int P>
+hipError_t launch_merge_t(const float* part_o, const float* part_ml, float* out, int H, int G, int S,
+                          int rows_per_head, int row_stride_out, long long rows, hipStream_t stream) {
+  const long long threads = rows * (D / 4) * P;
+  long long wgs = (threads + kMergeThreads - 1) / kMergeThreads;
+  if (wgs > kMergeMaxGrid) wgs = kMergeMaxGrid;  // larger merges stride over the rows
+  hipLaunchKernelGGL((merge_kernel<D, P>), dim3((unsigned)wgs), dim3(kMergeThreads), 0, stream, part_o, part_ml,
+                     out, H, G, S, rows_per_head, row_stride_out, rows);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_merge_d(const float* part_o, const float* part_ml, float* out, int H, int G, int S,
+                          int rows_per_head, int row_stride_out, long long rows, hipStream_t stream) {
+  // lanes per float4: the fewest that take every partial in one batch of loads
+  if (S <= 1 * kMergeBatch)
+    return launch_merge_t<D, 1>(part_o, part_ml, out, H, G, S, rows_per_head, row_stride_out, rows, stream);
+  if (S <= 2 * kMergeBatch)
+    return launch_merge_t<D, 2>(part_o, part_ml, out, H, G, S, rows_per_head, row_stride_out, rows, stream);
+  if (S <= 4 * kMergeBatch)
+    return launch_merge_t<D, 4>(part_o, part_ml, out, H, G, S, rows_per_head, row_stride_out, rows, stream);
+  if (S <= 8 * kMergeBatch)
+    return launch_merge_t<D, 8>(part_o, part_ml, out, H, G, S, rows_per_head, row_stride_out, rows, stream);
+  return launch_merge_t<D, kMergeMaxParts>(part_o, part_ml, out, H, G, S, rows_per_head, row_stride_out, rows,
+                                           stream);
 }
 
 template <typename T, int D, int NW>
@@ -136,17 +161,9 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_merge(const float* part_o, const float* part_ml, float* out, int R, int H, int G, int D, int S,
                         int rows_per_head, int row_stride_out, hipStream_t stream) {
   const long long rows = (long long)R * H * rows_per_head;
-  const long long threads = rows * (D / 4) * kMergeParts;
-  long long wgs = (threads + kMergeThreads - 1) / kMergeThreads;
-  if (wgs > kMergeMaxGrid) wgs = kMergeMaxGrid;  // larger merges stride over the rows
-  const dim3 grid((unsigned)wgs);
   if (D == 128)
-    hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(kMergeThreads), 0, stream, part_o, part_ml, out, H, G, S,
-                       rows_per_head, row_stride_out, rows);
-  else
-    hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(kMergeThreads), 0, stream, part_o, part_ml, out, H, G, S,
-                       rows_per_head, row_stride_out, rows);
-  return hipGetLastError();
+    return launch_merge_d<128>(part_o, part_ml, out, H, G, S, rows_per_head, row_stride_out, rows, stream);
+  return launch_merge_d<64>(part_o, part_ml, out, H, G, S, rows_per_head, row_stride_out, rows, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

@@ -226,33 +226,37 @@ __device__ __forceinline__ void wg_merge_store(WaveAttn<T, D>& st, MergeLds<NW, 
 // ------------------------------------------------------- partial merge
 //
 //   out[c] = sum_s 2^(m_s - m) o_s[c] / sum_s 2^(m_s - m) l_s,  m = max_s m_s.
-// kMergeParts consecutive lanes (one DPP row) share one output float4: lane
-// part p folds partials p, p + kMergeParts, p + 2 kMergeParts, ..., a batch
+// P consecutive lanes (P = 1, 2, 4, 8 or 16, within one DPP row) share one
+// output float4: lane part p folds partials p, p + P, p + 2 P, ..., a batch
 // of kMergeBatch at a time with all loads issued first, each batch weighted
 // against its own maximum (independent exponentials rather than a chain).
-// The sixteen lanes then agree on the row maximum by DPP exchanges, scale
-// their sums once, and add them by DPP exchanges (partners at xor 1 and 2,
-// then the half-row and row mirrors, which pair lanes of groups already
-// holding equal values).  Floating-point addition is commutative, so both
-// partners of an exchange form the same value; with no barrier, no LDS and a
-// fixed order of every sum, the result is deterministic.
-constexpr int kMergeParts = 16;  // lanes per output float4
-constexpr int kMergeBatch = 4;   // partials per lane per batch of loads
+// The launcher picks the smallest P whose lanes take all S partials in one
+// batch (16 beyond that).  The P lanes then agree on the group maximum by
+// DPP exchanges, scale their sums once, and add them by DPP exchanges
+// (partners at xor 1 and 2, then the half-row and row mirrors, which pair
+// lanes of groups already holding equal values).  Floating-point addition
+// is commutative, so both partners of an exchange form the same value; with
+// no barrier, no LDS and a fixed order of every sum, the result is
+// deterministic.
+constexpr int kMergeMaxParts = 16;  // lanes per output float4, at most
+constexpr int kMergeBatch = 4;      // partials per lane per batch of loads
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
-// Maximum, then sum, over the sixteen lanes of a DPP row.
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_f32<0xb1>(x));      // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp_f32<0x4e>(x));      // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_f32<0x141>(x));     // row_half_mirror
-  return fmaxf(x, dpp_f32<0x140>(x));  // row_mirror
+// Maximum over the P lanes of an aligned group, in every lane of it.
+template <int P>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (P >= 2) x = fmaxf(x, dpp_f32<0xb1>(x));   // quad_perm [1,0,3,2]
+  if constexpr (P >= 4) x = fmaxf(x, dpp_f32<0x4e>(x));   // quad_perm [2,3,0,1]
+  if constexpr (P >= 8) x = fmaxf(x, dpp_f32<0x141>(x));  // row_half_mirror
+  if constexpr (P >= 16) x = fmaxf(x, dpp_f32<0x140>(x)); // row_mirror
+  return x;
 }
 template <int CTRL>
-__device__ __forceinline__ void row16_add_step(float& l, floatx4_t& o) {
+__device__ __forceinline__ void group_add_step(float& l, floatx4_t& o) {
   l += dpp_f32<CTRL>(l);
 #pragma unroll
   for (int e = 0; e < 4; ++e) o[e] += dpp_f32<CTRL>(o[e]);
@@ -266,21 +270,20 @@ struct PlainPartials {
   __device__ floatx4_t load_o(size_t off) const { return *reinterpret_cast<const floatx4_t*>(o + off); }
 };
 
-// One output float4 (lane group of kMergeParts): S partials of partial row
-// `row` in the rows-per-partial layout (partial s, row: s * rows + row),
-// channels [4 c4, 4 c4 + 4).  Returns the merged float4 (in every lane of
-// the group).
-template <int D, class Parts>
+// One output float4 (lane group of P): S partials of partial row `row` in
+// the rows-per-partial layout (partial s, row: s * rows + row), channels
+// [4 c4, 4 c4 + 4).  Returns the merged float4 (in every lane of the group).
+template <int D, int P, class Parts>
 __device__ __forceinline__ floatx4_t merge_float4(const Parts& pp, size_t base, int S, int rows, int row, int c4,
                                                   int part) {
   float m_run = -INFINITY, l_run = 0.f;
   floatx4_t o_run = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = part; s0 < S; s0 += kMergeParts * kMergeBatch) {
+  for (int s0 = part; s0 < S; s0 += P * kMergeBatch) {
     float mv[kMergeBatch], lv[kMergeBatch];
     floatx4_t ov[kMergeBatch];
 #pragma unroll
     for (int b = 0; b < kMergeBatch; ++b) {
-      const int sp = s0 + b * kMergeParts;
+      const int sp = s0 + b * P;
       const bool ok = sp < S;
       const size_t pr = (base + (ok ? sp : 0)) * rows + row;
       const float2 ml = pp.load_ml(pr);
@@ -303,15 +306,15 @@ __device__ __forceinline__ floatx4_t merge_float4(const Parts& pp, size_t base, 
     }
     m_run = m_new;
   }
-  const float m_all = row16_max(m_run);
+  const float m_all = group_max<P>(m_run);
   const float m_use = m_all == -INFINITY ? 0.f : m_all;
   const float w = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_use);
   float l_sum = l_run * w;
   floatx4_t o_sum = o_run * w;
-  row16_add_step<0xb1>(l_sum, o_sum);
-  row16_add_step<0x4e>(l_sum, o_sum);
-  row16_add_step<0x141>(l_sum, o_sum);
-  row16_add_step<0x140>(l_sum, o_sum);
+  if constexpr (P >= 2) group_add_step<0xb1>(l_sum, o_sum);
+  if constexpr (P >= 4) group_add_step<0x4e>(l_sum, o_sum);
+  if constexpr (P >= 8) group_add_step<0x141>(l_sum, o_sum);
+  if constexpr (P >= 16) group_add_step<0x140>(l_sum, o_sum);
   const float inv = l_sum > 0.f ? 1.f / l_sum : 0.f;
   return o_sum * inv;
 }
