@@ -119,7 +119,7 @@ hipError_t launch_select(const ScoreArgs& a, hipStream_t stream);
 // sel_cnt, keys), `da` the attention's (splits, partials, out).  Whether
 // the fused launch serves these sizes (else the selection launch and the
 // decode launch run in its place):
-bool step_fused(int dtype, int key_stride, int max_sel, int splits);
+bool step_fused(int dtype, int key_stride, int max_sel, int splits, long long rows);
 hipError_t launch_step(const ScoreArgs& sa, const DecodeArgs& da, hipStream_t stream);
 
 // Log-sum-exp merge of split partials: out row (r, t, i*G + j) from

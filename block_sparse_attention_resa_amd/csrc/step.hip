@@ -28,8 +28,9 @@
 // the selection launch and the decode launch instead: rows of more than
 // 8192 keys (16 per thread; at 16384 keys the 256 workgroups' key reads
 // alone take about 4 us and the selection another 6 in every workgroup,
-// against 8.9 us for the whole selection launch on four CUs), fp32 caches,
-// and lists longer than the LDS list holds.  Every path gives the same
+// against 8.9 us for the whole selection launch on four CUs), grids of more
+// than 256 workgroups (they run in rounds, each repeating the selection's
+// latency), fp32 caches, and lists longer than the LDS list holds.  Every path gives the same
 // sel_idx and sel_cnt.
 #include "decode_core.h"
 
@@ -39,6 +40,7 @@ namespace {
 constexpr int kStepNW = kDecodeWaves;  // wavefronts of a select+attend workgroup
 constexpr int kStepNT = 64 * kStepNW;
 constexpr int kListCap = 2 * (kBins + 4);  // list entries the two selection histograms' LDS holds
+constexpr long long kStepFusedMaxWgs = 256;  // the fused grid's workgroups, at most: one per CU
 
 template <int NT, int NW, int D>
 struct SelDecodeLds {
@@ -173,15 +175,18 @@ hipError_t launch_select_decode_t(const ScoreArgs& sa, const DecodeArgs& da, int
 
 }  // namespace
 
-bool step_fused(int dtype, int key_stride, int max_sel, int splits) {
+bool step_fused(int dtype, int key_stride, int max_sel, int splits, long long rows) {
   const int bps = (max_sel + splits - 1) / splits;
-  return dtype == 0 && step_kpt(key_stride) > 0 && bps <= kListCap;
+  // The fused grid must fit one round of workgroups (one per CU): in a second
+  // round every workgroup's selection would sit on the critical path again
+  // (batch 128 x 2K: 45.0 against 42.8 us for the separate launches).
+  return dtype == 0 && step_kpt(key_stride) > 0 && bps <= kListCap && rows * splits <= kStepFusedMaxWgs;
 }
 
 hipError_t launch_step(const ScoreArgs& sa, const DecodeArgs& da, hipStream_t stream) {
   hipError_t e = launch_scores(sa, stream);
   if (e != hipSuccess) return e;
-  if (!step_fused(sa.dtype, sa.key_stride, sa.max_sel, da.splits)) {
+  if (!step_fused(sa.dtype, sa.key_stride, sa.max_sel, da.splits, (long long)da.R * da.H)) {
     e = launch_select(sa, stream);
     if (e != hipSuccess) return e;
     return launch_decode(da, stream);

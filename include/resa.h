@@ -220,9 +220,10 @@ resa_status resa_sparse_decode(const resa_config* cfg, const resa_paged_kv* kv,
  * attends over its own share of the selected list, then the merge of the
  * splits (split execution with a log-sum-exp merge: "Rectified Sparse
  * Attention" analysis page, §3.4.4; kernel time without CPU overhead: §5).
- * Rows of more than 8192 blocks (max_blocks), fp32 caches and lists whose
- * per-split share exceeds 8200 ids run the separate selection launch and
- * the decode launch instead.
+ * Rows of more than 8192 blocks (max_blocks), calls whose attention grid
+ * (requests x KV heads x splits) exceeds 256 workgroups, fp32 caches and
+ * lists whose per-split share exceeds 8200 ids run the separate selection
+ * launch and the decode launch instead.
  * Requires max_sel >= resa_selection_count(cfg, kv->max_blocks) and
  * ws_bytes >= resa_workspace_bytes(cfg, RESA_OP_SPARSE_STEP, num_requests,
  * kv->max_blocks, max_sel, 0); the workspace needs no initialisation.
