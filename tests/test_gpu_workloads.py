@@ -158,7 +158,7 @@ def graph_replay_case(spec, seeds, reps):
 def test_budget_sweep_64k(budget):
     """The budgets of the context x budget sweep besides 1/10, at 64K
     (4096 blocks per KV head; 82, 205 and 820 of them chosen): score/select +
-    sparse decode and the persistent step, selections and outputs against the
+    sparse decode and the step call, selections and outputs against the
     oracle, and the two paths against each other."""
     num, den = budget
     spec = WORKLOADS["qwen7b_ctx32k_b1"].with_(seq_lens=(65536,), budget_num=num, budget_den=den)
