@@ -101,6 +101,7 @@ def test_step_repeated_calls_on_one_workspace():
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name,seed,layer", [("qwen7b_ctx32k_b1", 101, 0), ("qwen7b_ragged_b8", 102, 0),
+                                             ("qwen7b_ctx131k_b4_rectify", 103, 0),
                                              ("qwen7b_ctx256k_l28", 2024, 0)])
 def test_step_full_size_workloads(name, seed, layer):
     spec = WORKLOADS[name]
