@@ -235,7 +235,9 @@ def test_split_count_changes_rounding_only():
 
 
 def test_many_splits_merge_batches():
-    """More splits than one lane group folds in one batch of loads (64), so the
+    """Split counts on both sides of every change of the merge's lanes per
+    output float4, one split (the decode writes the output, no merge), and
+    more splits than one lane group folds in one batch of loads (64), so the
     merge runs several batches; dense and all-blocks sparse decode against the
     oracle's dense attention."""
     case = make("bf16_d64_h2_g3")  # 5000 rows: 313 blocks
@@ -249,7 +251,10 @@ def test_many_splits_merge_batches():
     idx = torch.full((1, case.spec.num_kv_heads, M), -1, dtype=torch.int32, device="cuda")
     idx[0, :, :] = torch.arange(M, dtype=torch.int32, device="cuda")
     cnt = torch.full((1, case.spec.num_kv_heads), M, dtype=torch.int32, device="cuda")
-    for S in (65, 129, 200, M):
+    # every lanes-per-float4 boundary of the merge (1, 2, 4, 8, 16 lanes take
+    # up to 4, 8, 16, 32, 64 splits in one batch), one split (no merge), and
+    # several batches
+    for S in (1, 4, 5, 8, 9, 16, 17, 32, 33, 64, 65, 129, 200, M):
         case.cfg.num_splits = S
         de = C.run_dense(case)
         sp = C.run_sparse(case, idx, cnt)
