@@ -75,7 +75,10 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(
                            S == 1 ? out + ((size_t)r * H + i) * G * D : nullptr);
 }
 
-constexpr int kMergeThreads = 256;
+// one wavefront per merge workgroup: the merge is latency-bound, and small
+// workgroups spread its loads over more CUs (0.2-0.5 us per layer-step
+// against 256-thread workgroups at every size measured)
+constexpr int kMergeThreads = 64;
 constexpr long long kMergeMaxGrid = 1 << 20;  // workgroups of one merge launch
 
 // Log-sum-exp merge of split partials (decode_core.h), one output float4 per
