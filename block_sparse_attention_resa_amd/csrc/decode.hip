@@ -75,26 +75,41 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(
                            S == 1 ? out + ((size_t)r * H + i) * G * D : nullptr);
 }
 
-// one wavefront per merge workgroup: the merge is latency-bound, and small
-// workgroups spread its loads over more CUs (0.2-0.5 us per layer-step
-// against 256-thread workgroups at every size measured)
-constexpr int kMergeThreads = 64;
+// One wavefront per merge workgroup while the grid is small: the decode
+// merges are latency-bound, and small workgroups spread their loads over
+// more CUs (0.2-0.5 us per layer-step against 256-thread workgroups at every
+// decode size measured).  Merges of more than kMergeSmallMaxWgs wavefronts
+// (the rectification's) fill the chip either way and run 256-thread
+// workgroups.
+constexpr int kMergeSmallThreads = 64;
+constexpr int kMergeLargeThreads = 256;
+constexpr long long kMergeSmallMaxWgs = 2048;
 constexpr long long kMergeMaxGrid = 1 << 20;  // workgroups of one merge launch
+constexpr unsigned kXcds = 8;  // MI355X: 8 XCDs, each with its own L2; workgroups are dealt to them in turn
 
 // Log-sum-exp merge of split partials (decode_core.h), one output float4 per
 // P lanes.  64-bit thread index; the grid strides over the rows when it is
 // capped (rows * C4 * P may exceed 2^31).  The stride is a multiple of P, so
 // the P lanes of a group always share one row and leave the loop together.
-template <int D, int P>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part_o,
+template <int D, int P, int NTH>
+__global__ __launch_bounds__(NTH) void merge_kernel(const float* __restrict__ part_o,
                                                               const float* __restrict__ part_ml,
                                                               float* __restrict__ out, int H, int G, int S,
                                                               int rows_per_head, int row_stride_out,
                                                               long long total_rows) {
   constexpr int C4 = D / 4;  // float4 per output row
   const PlainPartials pp{part_o, part_ml};
-  const long long stride = (long long)gridDim.x * kMergeThreads;
-  for (long long g = (long long)blockIdx.x * kMergeThreads + threadIdx.x; g < total_rows * C4 * P; g += stride) {
+  // XCD-aware order: workgroup b runs on XCD b mod 8, so logical workgroups
+  // are numbered XCD by XCD (a bijection on the first 8 * (grid / 8)
+  // workgroups; the rest keep their index).  Neighbouring workgroups share
+  // 128-byte lines of the partials and the (m, l) pairs of their rows; on
+  // one XCD they fetch them from HBM once instead of once per L2.
+  const unsigned nwg = gridDim.x;
+  const unsigned full = nwg - nwg % kXcds;
+  const unsigned wg =
+      blockIdx.x < full ? (blockIdx.x % kXcds) * (full / kXcds) + blockIdx.x / kXcds : blockIdx.x;
+  const long long stride = (long long)nwg * NTH;
+  for (long long g = (long long)wg * NTH + threadIdx.x; g < total_rows * C4 * P; g += stride) {
     const int part = (int)(g % P);
     const int c4 = (int)((g / P) % C4);
     const long long grow = g / (P * C4);  // (r, i, row) flattened
@@ -116,10 +131,16 @@ template <int D, int P>
 hipError_t launch_merge_t(const float* part_o, const float* part_ml, float* out, int H, int G, int S,
                           int rows_per_head, int row_stride_out, long long rows, hipStream_t stream) {
   const long long threads = rows * (D / 4) * P;
-  long long wgs = (threads + kMergeThreads - 1) / kMergeThreads;
+  long long wgs = (threads + kMergeSmallThreads - 1) / kMergeSmallThreads;
+  if (wgs <= kMergeSmallMaxWgs) {
+    hipLaunchKernelGGL((merge_kernel<D, P, kMergeSmallThreads>), dim3((unsigned)wgs), dim3(kMergeSmallThreads), 0,
+                       stream, part_o, part_ml, out, H, G, S, rows_per_head, row_stride_out, rows);
+    return hipGetLastError();
+  }
+  wgs = (threads + kMergeLargeThreads - 1) / kMergeLargeThreads;
   if (wgs > kMergeMaxGrid) wgs = kMergeMaxGrid;  // larger merges stride over the rows
-  hipLaunchKernelGGL((merge_kernel<D, P>), dim3((unsigned)wgs), dim3(kMergeThreads), 0, stream, part_o, part_ml,
-                     out, H, G, S, rows_per_head, row_stride_out, rows);
+  hipLaunchKernelGGL((merge_kernel<D, P, kMergeLargeThreads>), dim3((unsigned)wgs), dim3(kMergeLargeThreads), 0,
+                     stream, part_o, part_ml, out, H, G, S, rows_per_head, row_stride_out, rows);
   return hipGetLastError();
 }
 
