@@ -29,12 +29,13 @@ namespace resa {
 namespace {
 
 constexpr int kScoreFill = 256;     // scoring workgroups that keep the 256 CUs busy
+constexpr long long kScoreFill8 = 640;  // scoring workgroups at eight passes from which eight are used
 constexpr int kScoreThreads = 256;  // threads of a scoring workgroup, at most
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectSmall = 512;  // threads of the selection of rows of up to 4096 keys
 
 // U: blocks per thread (passes), 4, or 2 or 1 for grids too small to give
-// every CU a workgroup at 4.
+// every CU a workgroup at 4, or 8 for grids large at 8 too.
 template <typename T, int D, int MODE, int MAXG, int U>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const T* __restrict__ q, const T* desc, const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
@@ -267,9 +268,16 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
   const int threads = unit * m;  // <= kScoreThreads
   const int bpi = m;
   // Four passes per thread, unless the grid would then leave CUs idle (short
-  // rows, few requests): fewer passes and more workgroups there.
+  // rows, few requests): fewer passes and more workgroups there.  Large
+  // grids (long rows of several requests) take eight: each workgroup's fixed
+  // cost (table entries, query fold, barrier) is then spread over twice the
+  // descriptors (per layer-step: ragged 8 x 32-64K 44.3 -> 43.5 us, 4 x 131K
+  // 51.2 -> 50.9, 128 x 2K 42.8 -> 42.1; sixteen passes were slower, and
+  // grids below kScoreFill8 at eight passes, such as one 256K request or 64
+  // requests of 4K, gain nothing).
   const long long groups = (long long)a.R * ((a.H + HW - 1) / HW);
   int U = 4;
+  if (bpi * 8 <= 64 && groups * ((a.max_blocks + bpi * 8 - 1) / (bpi * 8)) >= kScoreFill8) U = 8;
   while (U > 1 && groups * ((a.max_blocks + bpi * U - 1) / (bpi * U)) < kScoreFill) U /= 2;
   const int blocks_per_wg = bpi * U;  // <= 64: one table entry per lane
   const int wgs = (a.max_blocks + blocks_per_wg - 1) / blocks_per_wg;
@@ -282,7 +290,8 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t stream) {
                      static_cast<T*>(const_cast<void*>(a.desc_pool)), wgs, a.key_stride)
 #define RESA_SCORE_LAUNCH(MODE, MAXG)                      \
   do {                                                     \
-    if (U == 4) RESA_SCORE_LAUNCH_U(MODE, MAXG, 4);        \
+    if (U == 8) RESA_SCORE_LAUNCH_U(MODE, MAXG, 8);        \
+    else if (U == 4) RESA_SCORE_LAUNCH_U(MODE, MAXG, 4);   \
     else if (U == 2) RESA_SCORE_LAUNCH_U(MODE, MAXG, 2);   \
     else RESA_SCORE_LAUNCH_U(MODE, MAXG, 1);               \
   } while (0)
